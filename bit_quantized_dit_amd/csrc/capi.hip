@@ -1,0 +1,291 @@
+// C-ABI front end of the W4A4 library: argument validation, size queries, blob and
+// workspace layout, the host half of offline calibration, and kernel dispatch.
+// The operations and their page citations are documented in include/w4a4.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "w4a4_internal.h"
+
+using namespace w4a4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+int dev_status(hipError_t e) { return e == hipSuccess ? W4A4_OK : W4A4_ERR_DEVICE; }
+
+int64_t weight_scale_bytes(int64_t d_out, int64_t k_pad, int layout) {
+    if (layout == W4A4_WS_1X32) return d_out * (k_pad / 32);
+    if (layout == W4A4_WS_128X1_STRIPE) return d_out * (k_pad / 128);
+    return (k_pad / 32) * ((d_out + 31) / 32);
+}
+
+struct BlobLayout {
+    size_t colmap, s, O, J, B_q, B_s, W_O, total;
+};
+
+BlobLayout blob_layout(int64_t d_in, int64_t d_out, int32_t k, int layout) {
+    const int64_t k_j = d_in - k;
+    const int64_t k_pad = round_up(k_j, 128);
+    const int64_t k_ld = round_up(k, 32);
+    BlobLayout b;
+    size_t off = 0;
+    b.colmap = off; off = align_up(off + (size_t)d_in * 4);
+    b.s = off;      off = align_up(off + (size_t)d_in * 4);
+    b.O = off;      off = align_up(off + (size_t)k * 4);
+    b.J = off;      off = align_up(off + (size_t)k_j * 4);
+    b.B_q = off;    off = align_up(off + (size_t)(d_out * (k_pad / 2)));
+    b.B_s = off;    off = align_up(off + (size_t)weight_scale_bytes(d_out, k_pad, layout));
+    b.W_O = off;    off = align_up(off + (size_t)(d_out * k_ld) * 2);
+    b.total = off;
+    return b;
+}
+
+bool valid_layout(int layout) {
+    return layout == W4A4_WS_1X32 || layout == W4A4_WS_32X32_TILE || layout == W4A4_WS_128X1_STRIPE;
+}
+
+int check_dims(int64_t d_in, int64_t d_out, int32_t k, int layout) {
+    if (!valid_layout(layout)) return W4A4_ERR_INVALID;
+    if (d_in <= 0 || d_out <= 0 || k < 0 || k > d_in) return W4A4_ERR_INVALID;
+    if (d_in > W4A4_MAX_D_IN) return W4A4_ERR_SHAPE;
+    if (d_out > ((int64_t)1 << 30)) return W4A4_ERR_SHAPE;
+    return W4A4_OK;
+}
+
+int check_desc(const w4a4_packed* d) {
+    if (!d) return W4A4_ERR_INVALID;
+    int st = check_dims(d->d_in, d->d_out, d->k, d->layout);
+    if (st) return st;
+    if (d->k_j != d->d_in - d->k || d->k_pad != round_up(d->k_j, 128) || d->k_ld != round_up(d->k, 32))
+        return W4A4_ERR_INVALID;
+    if (!d->colmap || !d->s) return W4A4_ERR_INVALID;
+    if (d->k_pad > 0 && (!d->B_q || !d->B_s || !d->J)) return W4A4_ERR_INVALID;
+    if (d->k > 0 && (!d->W_O || !d->O)) return W4A4_ERR_INVALID;
+    if (misaligned(d->colmap) || misaligned(d->s) || misaligned(d->B_q) || misaligned(d->W_O))
+        return W4A4_ERR_ALIGN;
+    return W4A4_OK;
+}
+
+w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) {
+    w4a4_ws_layout w;
+    size_t off = 0;
+    w.a_q = off; off = align_up(off + (size_t)(T * (d->k_pad / 2)));
+    w.a_s = off; off = align_up(off + (size_t)(T * (d->k_pad / 32)));
+    w.x_o = off; off = align_up(off + (size_t)(T * d->k_ld) * 2);
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a4_status_string(int status) {
+    switch (status) {
+        case W4A4_OK: return "ok";
+        case W4A4_ERR_INVALID: return "invalid argument";
+        case W4A4_ERR_SHAPE: return "unsupported shape or buffer too small";
+        case W4A4_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case W4A4_ERR_DEVICE: return "HIP runtime error";
+        case W4A4_ERR_NONFINITE: return "non-finite calibration data";
+        default: return "unknown status";
+    }
+}
+
+int w4a4_column_absmax(const void* X, int x_dtype, int64_t rows, int64_t cols, uint32_t* out_bits,
+                       void* stream) {
+    if (!X || !out_bits || rows < 0 || cols < 0) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    return dev_status(launch_column_absmax(X, x_dtype, rows, cols, out_bits, (hipStream_t)stream));
+}
+
+int w4a4_calibrate_scales(const void* X_cal, int x_dtype, int64_t T_cal, int64_t d_in, const float* W,
+                          int64_t d_out, float alpha, int32_t k, float* s_out, int32_t* O_out,
+                          float* act_scale_out, float* weight_scale_out, void* stream) {
+    if (!X_cal || !W || !s_out || (k > 0 && !O_out)) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    if (T_cal <= 0 || d_in <= 0 || d_out <= 0 || k < 0 || k > d_in) return W4A4_ERR_INVALID;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return W4A4_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t* dev = nullptr;
+    if (hipMalloc(&dev, (size_t)d_in * 2 * sizeof(uint32_t)) != hipSuccess) return W4A4_ERR_DEVICE;
+    std::vector<uint32_t> bits((size_t)d_in * 2);
+    hipError_t e = launch_column_absmax(X_cal, x_dtype, T_cal, d_in, dev, st);
+    if (e == hipSuccess) e = launch_column_absmax(W, W4A4_X_F32, d_out, d_in, dev + d_in, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(bits.data(), dev, bits.size() * sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    (void)hipFree(dev);
+    if (e != hipSuccess) return W4A4_ERR_DEVICE;
+
+    std::vector<float> act((size_t)d_in), wsc((size_t)d_in);
+    for (int64_t j = 0; j < d_in; ++j) {
+        if (bits[j] >= 0x7F800000u || bits[d_in + j] >= 0x7F800000u) return W4A4_ERR_NONFINITE;
+        std::memcpy(&act[j], &bits[j], 4);
+        std::memcpy(&wsc[j], &bits[d_in + j], 4);
+    }
+    // s_j = a^alpha / w^(1-alpha) (sec. 3.2), maxima floored at 1e-5, double, one rounding.
+    const float floor_v = 1e-5f;
+    std::vector<float> score((size_t)d_in);
+    for (int64_t j = 0; j < d_in; ++j) {
+        const float a = act[j] > floor_v ? act[j] : floor_v;
+        const float w = wsc[j] > floor_v ? wsc[j] : floor_v;
+        const double num = std::pow((double)a, (double)alpha);
+        const double den = std::pow((double)w, 1.0 - (double)alpha);
+        s_out[j] = (float)(num / den);
+        score[j] = act[j] / s_out[j];   // = max_t |x_tj / s_j| (binary32 division is monotone)
+    }
+    if (act_scale_out) std::memcpy(act_scale_out, act.data(), (size_t)d_in * 4);
+    if (weight_scale_out) std::memcpy(weight_scale_out, wsc.data(), (size_t)d_in * 4);
+    // static top-k (sec. 3.3): larger score first, ties to the smaller column
+    std::vector<int32_t> idx((size_t)d_in);
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return score[x] > score[y]; });
+    std::sort(idx.begin(), idx.begin() + k);
+    for (int32_t i = 0; i < k; ++i) O_out[i] = idx[i];
+    return W4A4_OK;
+}
+
+int w4a4_packed_size(int64_t d_in, int64_t d_out, int32_t k, int layout, size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    const int st = check_dims(d_in, d_out, k, layout);
+    if (st) return st;
+    *bytes = blob_layout(d_in, d_out, k, layout).total;
+    return W4A4_OK;
+}
+
+int w4a4_pack_weights(const float* W, int64_t d_in, int64_t d_out, const float* s, const int32_t* O,
+                      int32_t k, int layout, void* blob, size_t blob_bytes, w4a4_packed* desc,
+                      void* stream) {
+    if (!W || !s || !blob || !desc || (k > 0 && !O)) return W4A4_ERR_INVALID;
+    int st = check_dims(d_in, d_out, k, layout);
+    if (st) return st;
+    if (((uintptr_t)W & 3u) != 0 || misaligned(blob)) return W4A4_ERR_ALIGN;
+    const BlobLayout b = blob_layout(d_in, d_out, k, layout);
+    if (blob_bytes < b.total) return W4A4_ERR_SHAPE;
+    for (int64_t j = 0; j < d_in; ++j)
+        if (!(s[j] > 0.0f) || !std::isfinite(s[j])) return W4A4_ERR_INVALID;
+    for (int32_t i = 0; i < k; ++i) {
+        if (O[i] < 0 || O[i] >= d_in) return W4A4_ERR_INVALID;
+        if (i > 0 && O[i] <= O[i - 1]) return W4A4_ERR_INVALID;
+    }
+    const int64_t k_j = d_in - k;
+    std::vector<int32_t> colmap((size_t)d_in), J((size_t)k_j);
+    {
+        int32_t io = 0, p = 0;
+        for (int64_t j = 0; j < d_in; ++j) {
+            if (io < k && O[io] == j) { colmap[j] = -(io + 1); ++io; }
+            else { colmap[j] = p; J[p] = (int32_t)j; ++p; }
+        }
+    }
+    uint8_t* base = (uint8_t*)blob;
+    w4a4_packed d;
+    d.d_in = d_in;
+    d.d_out = d_out;
+    d.k = k;
+    d.layout = layout;
+    d.k_j = k_j;
+    d.k_pad = round_up(k_j, 128);
+    d.k_ld = round_up(k, 32);
+    d.colmap = (const int32_t*)(base + b.colmap);
+    d.s = (const float*)(base + b.s);
+    d.O = (const int32_t*)(base + b.O);
+    d.J = (const int32_t*)(base + b.J);
+    d.B_q = base + b.B_q;
+    d.B_s = base + b.B_s;
+    d.W_O = (const uint16_t*)(base + b.W_O);
+
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync((void*)d.colmap, colmap.data(), (size_t)d_in * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync((void*)d.s, s, (size_t)d_in * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess && k > 0) e = hipMemcpyAsync((void*)d.O, O, (size_t)k * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess && k_j > 0)
+        e = hipMemcpyAsync((void*)d.J, J.data(), (size_t)k_j * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = launch_pack(W, d, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return W4A4_ERR_DEVICE;
+    *desc = d;
+    return W4A4_OK;
+}
+
+int w4a4_workspace_layout(int64_t T, const w4a4_packed* desc, w4a4_ws_layout* out) {
+    if (!out || T < 0) return W4A4_ERR_INVALID;
+    const int st = check_desc(desc);
+    if (st) return st;
+    *out = ws_layout(T, desc);
+    return W4A4_OK;
+}
+
+int w4a4_workspace_size(int64_t T, const w4a4_packed* desc, size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    w4a4_ws_layout w;
+    const int st = w4a4_workspace_layout(T, desc, &w);
+    if (st) return st;
+    *bytes = w.total;
+    return W4A4_OK;
+}
+
+int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, void* ws,
+                              size_t ws_bytes, void* stream) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    int st = check_desc(desc);
+    if (st) return st;
+    if (T == 0) return W4A4_OK;
+    if (!X || !ws) return W4A4_ERR_INVALID;
+    if (misaligned(X) || misaligned(ws)) return W4A4_ERR_ALIGN;
+    const w4a4_ws_layout w = ws_layout(T, desc);
+    if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
+    uint8_t* b = (uint8_t*)ws;
+    return dev_status(launch_actprep(X, x_dtype, T, *desc, b + w.a_q, b + w.a_s, (uint16_t*)(b + w.x_o),
+                                     (hipStream_t)stream));
+}
+
+int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
+                           void* stream) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    int st = check_desc(desc);
+    if (st) return st;
+    if (T == 0) return W4A4_OK;
+    if (!ws || !Y) return W4A4_ERR_INVALID;
+    if (misaligned(ws) || misaligned(Y)) return W4A4_ERR_ALIGN;
+    const w4a4_ws_layout w = ws_layout(T, desc);
+    if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
+    const uint8_t* b = (const uint8_t*)ws;
+    return dev_status(launch_gemm(b + w.a_q, b + w.a_s, (const uint16_t*)(b + w.x_o), T, *desc, Y,
+                                  (hipStream_t)stream));
+}
+
+int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y, void* ws,
+                size_t ws_bytes, void* stream) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    int st = check_desc(desc);
+    if (st) return st;
+    if (T == 0) return W4A4_OK;
+    if (!Y) return W4A4_ERR_INVALID;
+    if (misaligned(Y)) return W4A4_ERR_ALIGN;
+    st = w4a4_quantize_activations(X, x_dtype, T, desc, ws, ws_bytes, stream);
+    if (st) return st;
+    return w4a4_gemm_prequantized(ws, ws_bytes, T, desc, Y, stream);
+}
+
+int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream) {
+    if (n < 0) return W4A4_ERR_INVALID;
+    if (n == 0) return W4A4_OK;
+    if (!Y || !H) return W4A4_ERR_INVALID;
+    if (misaligned(Y) || misaligned(H)) return W4A4_ERR_ALIGN;
+    return dev_status(launch_gelu(Y, n, H, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Device-side helpers shared by the gfx950 kernels of the W4A4 library.
+//
+// MXFP4 encoding used throughout (format named by "W4A4 Quantization for
+// Inference on Wan2.2-I2V-A14B (ICME 2026 Challenge)", sec. 1-2, OCP MX
+// definition):
+//   scale  E8M0 code c, value 2^(c-127); for a group with largest magnitude
+//          amax: c = max(biased_exponent(amax) - 2, 0), i.e.
+//          E = floor(log2 amax) - 2 clamped at -127 (subnormal and zero amax
+//          give c = 0); NaN/Inf anywhere in the group gives c = 0xFF.
+//   element E2M1 nibble: magnitude code = nearest of {0,.5,1,1.5,2,3,4,6} to
+//          |x| * 2^-E, ties to the even code, saturating at 6; bit 3 = sign of x.
+//
+// Taking the group maximum on the integer bit patterns of |x| makes NaN/Inf
+// detection free: any such element has abs bits >= 0x7F800000, which forces
+// the exponent field of the maximum to 0xFF.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// E8M0 code from the bit pattern of the group's largest |x|.
+__device__ __forceinline__ uint32_t e8m0_from_absbits(uint32_t amax_bits) {
+    const uint32_t e = amax_bits >> 23;
+    return e == 0xFFu ? 0xFFu : (e > 2u ? e - 2u : 0u);
+}
+
+// 2^-E as a binary32 for a finite scale code c (c <= 252 for finite amax, so the
+// biased exponent 254 - c stays in [2, 254]).
+__device__ __forceinline__ float e8m0_inverse(uint32_t c) { return __uint_as_float((254u - c) << 23); }
+
+// E2M1 nibble of x under the inverse scale `inv` (a power of two, so |x| * inv is
+// exact whenever it is a normal number; below 2^-126 every rounding gives code 0).
+__device__ __forceinline__ uint32_t e2m1_nibble(float x, float inv) {
+    const float m = __builtin_fabsf(x) * inv;
+    uint32_t c = (m > 0.25f) ? 1u : 0u;
+    c += (m >= 0.75f) ? 1u : 0u;
+    c += (m > 1.25f) ? 1u : 0u;
+    c += (m >= 1.75f) ? 1u : 0u;
+    c += (m > 2.5f) ? 1u : 0u;
+    c += (m >= 3.5f) ? 1u : 0u;
+    c += (m > 5.0f) ? 1u : 0u;
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// binary32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+}  // namespace w4a4

@@ -1,0 +1,24 @@
+// Internal launchers shared between the C-ABI front end and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a4.h"
+
+namespace w4a4 {
+
+hipError_t launch_column_absmax(const void* X, int x_dtype, int64_t rows, int64_t cols,
+                                uint32_t* out_bits, hipStream_t st);
+
+hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st);
+
+hipError_t launch_actprep(const void* X, int x_dtype, int64_t T, const w4a4_packed& d,
+                          uint8_t* Aq, uint8_t* As, uint16_t* XO, hipStream_t st);
+
+hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
+                       const w4a4_packed& d, float* Y, hipStream_t st);
+
+hipError_t launch_gelu(const float* Y, int64_t n, uint16_t* H, hipStream_t st);
+
+}  // namespace w4a4

@@ -54,11 +54,12 @@ WORKLOADS = {
 }
 # Full FFN block at 57600 tokens: up as workload 4 but with 32x32 weight tiles, then
 # GELU-tanh, then the down projection 13824->5120 (k=64, alpha 0.5, 128x1 stripes).
+# The block's input activations and up weights are workload 4's draws (same seed).
 FFN_BLOCK = {
     "up": LayerSpec("ffn_block_up_T57600_5120x13824_k128", 57600, 5120, 13824, 128, 0.7, 1,
-                    "bf16", "normal_t3", 128, 0.02, None, 1024, 5000),
+                    "bf16", "normal_t3", 128, 0.02, None, 1024, 4000),
     "down": LayerSpec("ffn_block_down_T57600_13824x5120_k64", 57600, 13824, 5120, 64, 0.5, 2,
-                      "bf16", "from_up", 0, 0.01, None, 1024, 5000),
+                      "bf16", "from_up", 0, 0.01, None, 1024, 4000),
 }
 
 

@@ -1,0 +1,285 @@
+"""ctypes binding of libw4a4.so (argument marshalling only).
+
+Every function carries the name of the C entry point it wraps (see include/w4a4.h for
+the operations and their citations).  Torch tensors serve only as device buffers and
+their current HIP stream; every step of the computation runs in the library's
+kernels.  If the library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a4.so")
+
+W4A4_X_F32 = 0
+W4A4_X_BF16 = 1
+W4A4_WS_1X32 = 0
+W4A4_WS_32X32_TILE = 1
+W4A4_WS_128X1_STRIPE = 2
+STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR_ALIGN",
+          4: "W4A4_ERR_DEVICE", 5: "W4A4_ERR_NONFINITE"}
+
+EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", "w4a4_packed_size",
+           "w4a4_pack_weights", "w4a4_workspace_layout", "w4a4_workspace_size",
+           "w4a4_quantize_activations", "w4a4_gemm_prequantized", "w4a4_linear",
+           "w4a4_gelu_tanh_bf16")
+
+
+class W4A4Packed(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64), ("k", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("k_j", ctypes.c_int64), ("k_pad", ctypes.c_int64),
+                ("k_ld", ctypes.c_int64), ("colmap", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("O", ctypes.c_void_p), ("J", ctypes.c_void_p), ("B_q", ctypes.c_void_p),
+                ("B_s", ctypes.c_void_p), ("W_O", ctypes.c_void_p)]
+
+
+class W4A4WsLayout(ctypes.Structure):
+    _fields_ = [("a_q", ctypes.c_size_t), ("a_s", ctypes.c_size_t), ("x_o", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a4.so; raise if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_dit_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        ci, f32 = ctypes.c_int, ctypes.c_float
+        P = ctypes.POINTER
+        sig = {
+            "w4a4_status_string": (ctypes.c_char_p, [ci]),
+            "w4a4_column_absmax": (ci, [vp, ci, i64, i64, vp, vp]),
+            "w4a4_calibrate_scales": (ci, [vp, ci, i64, i64, vp, i64, f32, i32, vp, vp, vp, vp, vp]),
+            "w4a4_packed_size": (ci, [i64, i64, i32, ci, P(sz)]),
+            "w4a4_pack_weights": (ci, [vp, i64, i64, vp, vp, i32, ci, vp, sz, P(W4A4Packed), vp]),
+            "w4a4_workspace_layout": (ci, [i64, P(W4A4Packed), P(W4A4WsLayout)]),
+            "w4a4_workspace_size": (ci, [i64, P(W4A4Packed), P(sz)]),
+            "w4a4_quantize_activations": (ci, [vp, ci, i64, P(W4A4Packed), vp, sz, vp]),
+            "w4a4_gemm_prequantized": (ci, [vp, sz, i64, P(W4A4Packed), vp, vp]),
+            "w4a4_linear": (ci, [vp, ci, i64, P(W4A4Packed), vp, vp, sz, vp]),
+            "w4a4_gelu_tanh_bf16": (ci, [vp, i64, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().w4a4_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS.get(status, "?")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise W4A4Error(fn, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _x_dtype(X: torch.Tensor) -> int:
+    if X.dtype == torch.float32:
+        return W4A4_X_F32
+    if X.dtype == torch.bfloat16:
+        return W4A4_X_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {X.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedLayer:
+    """A packed layer: the device blob (kept alive here) and its descriptor."""
+    blob: torch.Tensor
+    desc: W4A4Packed
+
+    @property
+    def d_in(self) -> int: return self.desc.d_in
+    @property
+    def d_out(self) -> int: return self.desc.d_out
+    @property
+    def k(self) -> int: return self.desc.k
+    @property
+    def k_pad(self) -> int: return self.desc.k_pad
+    @property
+    def k_ld(self) -> int: return self.desc.k_ld
+    @property
+    def layout(self) -> int: return self.desc.layout
+
+    def views(self) -> dict:
+        """Device views of the packed arrays inside the blob."""
+        base = self.blob.data_ptr()
+        d = self.desc
+
+        def view(ptr, nbytes, dtype, shape):
+            off = ptr - base
+            return self.blob[off:off + nbytes].view(dtype).view(*shape)
+        if d.layout == W4A4_WS_1X32:
+            bs_shape = (d.d_out, d.k_pad // 32)
+        elif d.layout == W4A4_WS_128X1_STRIPE:
+            bs_shape = (d.d_out, d.k_pad // 128)
+        else:
+            bs_shape = (d.k_pad // 32, (d.d_out + 31) // 32)
+        out = {"colmap": view(d.colmap, d.d_in * 4, torch.int32, (d.d_in,)),
+               "s": view(d.s, d.d_in * 4, torch.float32, (d.d_in,))}
+        if d.k_pad:
+            out["B_q"] = view(d.B_q, d.d_out * d.k_pad // 2, torch.uint8, (d.d_out, d.k_pad // 2))
+            out["B_s"] = view(d.B_s, bs_shape[0] * bs_shape[1], torch.uint8, bs_shape)
+            out["J"] = view(d.J, d.k_j * 4, torch.int32, (d.k_j,))
+        if d.k:
+            out["W_O"] = view(d.W_O, d.d_out * d.k_ld * 2, torch.bfloat16, (d.d_out, d.k_ld))
+            out["O"] = view(d.O, d.k * 4, torch.int32, (d.k,))
+        return out
+
+
+# --------------------------------------------------------------------------- calls
+
+def w4a4_column_absmax(X: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev(X, "X")
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty(cols, dtype=torch.int32, device=X.device)
+    _check("w4a4_column_absmax", lib().w4a4_column_absmax(_ptr(X), _x_dtype(X), rows, cols, _ptr(out),
+                                                           _stream(stream)))
+    return out
+
+
+def w4a4_calibrate_scales(X_cal: torch.Tensor, W: torch.Tensor, alpha: float, k: int, stream=None):
+    """Returns (s, O, act_scale, weight_scale) as host numpy arrays."""
+    _dev(X_cal, "X_cal")
+    _dev(W, "W")
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    T_cal, d_in = X_cal.shape
+    d_out = W.shape[0]
+    if W.shape[1] != d_in:
+        raise ValueError("W must be [d_out, d_in]")
+    s = np.zeros(d_in, np.float32)
+    O = np.zeros(max(k, 1), np.int32)
+    a = np.zeros(d_in, np.float32)
+    w = np.zeros(d_in, np.float32)
+    vp = lambda arr: arr.ctypes.data_as(ctypes.c_void_p)
+    st = lib().w4a4_calibrate_scales(_ptr(X_cal), _x_dtype(X_cal), T_cal, d_in, _ptr(W), d_out,
+                                     float(alpha), int(k), vp(s), vp(O), vp(a), vp(w), _stream(stream))
+    _check("w4a4_calibrate_scales", st)
+    return s, O[:k].copy(), a, w
+
+
+def w4a4_packed_size(d_in: int, d_out: int, k: int, layout: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4a4_packed_size", lib().w4a4_packed_size(d_in, d_out, k, layout, ctypes.byref(n)))
+    return n.value
+
+
+def w4a4_pack_weights(W: torch.Tensor, s: np.ndarray, O: np.ndarray, layout: int,
+                      stream=None) -> PackedLayer:
+    _dev(W, "W")
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    d_out, d_in = W.shape
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    O = np.ascontiguousarray(O, dtype=np.int32)
+    k = int(O.size)
+    nbytes = w4a4_packed_size(d_in, d_out, k, layout)
+    blob = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=W.device)
+    desc = W4A4Packed()
+    Optr = O.ctypes.data_as(ctypes.c_void_p) if k else None
+    st = lib().w4a4_pack_weights(_ptr(W), d_in, d_out, s.ctypes.data_as(ctypes.c_void_p), Optr, k,
+                                 int(layout), _ptr(blob), blob.numel(), ctypes.byref(desc),
+                                 _stream(stream))
+    _check("w4a4_pack_weights", st)
+    return PackedLayer(blob, desc)
+
+
+def w4a4_workspace_layout(T: int, packed: PackedLayer) -> W4A4WsLayout:
+    out = W4A4WsLayout()
+    _check("w4a4_workspace_layout",
+           lib().w4a4_workspace_layout(T, ctypes.byref(packed.desc), ctypes.byref(out)))
+    return out
+
+
+def w4a4_workspace_size(T: int, packed: PackedLayer) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4a4_workspace_size", lib().w4a4_workspace_size(T, ctypes.byref(packed.desc), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(T: int, packed: PackedLayer, device="cuda") -> torch.Tensor:
+    return torch.empty(max(w4a4_workspace_size(T, packed), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_views(ws: torch.Tensor, T: int, packed: PackedLayer) -> dict:
+    """Device views of A_q [T, k_pad/2], A_s [T, k_pad/32] and X_O [T, k_ld] inside ws."""
+    L = w4a4_workspace_layout(T, packed)
+    kp, kl = packed.k_pad, packed.k_ld
+    return {"A_q": ws[L.a_q:L.a_q + T * kp // 2].view(T, kp // 2),
+            "A_s": ws[L.a_s:L.a_s + T * kp // 32].view(T, kp // 32),
+            "X_O": ws[L.x_o:L.x_o + T * kl * 2].view(torch.bfloat16).view(T, kl)}
+
+
+def w4a4_quantize_activations(X: torch.Tensor, packed: PackedLayer, ws: torch.Tensor, stream=None) -> None:
+    _dev(X, "X")
+    T = X.shape[0]
+    st = lib().w4a4_quantize_activations(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(ws),
+                                         ws.numel(), _stream(stream))
+    _check("w4a4_quantize_activations", st)
+
+
+def w4a4_gemm_prequantized(ws: torch.Tensor, T: int, packed: PackedLayer, Y: torch.Tensor,
+                           stream=None) -> None:
+    _dev(Y, "Y")
+    st = lib().w4a4_gemm_prequantized(_ptr(ws), ws.numel(), T, ctypes.byref(packed.desc), _ptr(Y),
+                                      _stream(stream))
+    _check("w4a4_gemm_prequantized", st)
+
+
+def w4a4_linear(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, ws: torch.Tensor,
+                stream=None) -> None:
+    _dev(X, "X")
+    _dev(Y, "Y")
+    T = X.shape[0]
+    st = lib().w4a4_linear(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
+                           ws.numel(), _stream(stream))
+    _check("w4a4_linear", st)
+
+
+def w4a4_gelu_tanh_bf16(Y: torch.Tensor, H: torch.Tensor, stream=None) -> None:
+    _dev(Y, "Y")
+    _dev(H, "H")
+    st = lib().w4a4_gelu_tanh_bf16(_ptr(Y), Y.numel(), _ptr(H), _stream(stream))
+    _check("w4a4_gelu_tanh_bf16", st)

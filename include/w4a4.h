@@ -1,0 +1,170 @@
+/*
+ * w4a4.h -- C ABI of the MI355X (gfx950) W4A4 dual-branch linear library.
+ *
+ * The layer (page "W4A4 Quantization for Inference on Wan2.2-I2V-A14B (ICME 2026
+ * Challenge)", xllm-io paper review, sec. 3.2-3.4):
+ *
+ *     Y = Q(X_J / s_J) . Q(s_J * W_J)  +  X_O . W_O
+ *
+ *   - SmoothQuant smoothing s_j = act_scale_j^alpha / weight_scale_j^(1-alpha)
+ *     (sec. 3.2), folded into the weights offline; activations are divided by s
+ *     at inference time and then quantized.
+ *   - A static set O of k outlier input columns, the top-k of
+ *     score_j = max_t |x_tj / s_j| over calibration tokens (sec. 3.3, scored
+ *     after the fold per sec. 3.5), runs as a narrow BF16 branch on the raw
+ *     (unsmoothed) columns; the rest, J, runs as strict MXFP4.
+ *   - MXFP4 (named in sec. 1-2; OCP MX definition): E2M1 codes
+ *     {0,+-0.5,+-1,+-1.5,+-2,+-3,+-4,+-6}, two per byte with the even K index
+ *     in the low nibble, one E8M0 scale 2^(code-127) per group;
+ *     E = floor(log2 amax) - 2 clamped at -127, amax = 0 -> code 0, a NaN/Inf
+ *     in the group -> code 0xFF with all its nibbles 0; elements round to
+ *     nearest, ties to the even code, saturating at 6, sign kept.
+ *   - Weight scale groups (sec. 3.4): 1x32 along K, 32x32 tiles, or 128x1
+ *     K-major stripes.  Activation scales are always 1x32 per token.
+ *   - The J columns are compacted in ascending order and zero padded to
+ *     K_pad = roundup(K_J, 128), K_J = d_in - k.
+ *
+ * Conventions for every entry point:
+ *   - Return value: a w4a4_status; no exception or abort crosses the ABI.
+ *   - "device" pointers are HIP device memory on the current device; "host"
+ *     pointers are ordinary host memory.  The caller owns every buffer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls marked async only enqueue work on it; kernel faults surface at the
+ *     caller's next synchronisation as HIP errors.
+ *   - Shapes are validated before anything is enqueued.  T = 0 is a no-op.
+ *   - Device pointers handed to the per-call entry points must be 16-byte
+ *     aligned; buffers sized by the size queries are 256-byte aligned inside.
+ *   - Calls on different streams that share a workspace race; the library keeps
+ *     no global state and is otherwise reentrant.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4a4_status {
+    W4A4_OK = 0,
+    W4A4_ERR_INVALID = 1,   /* null pointer, bad dtype/layout, k not in [0,d_in], alpha not in [0,1], negative size */
+    W4A4_ERR_SHAPE = 2,     /* size beyond the supported range, or a blob/workspace that is too small */
+    W4A4_ERR_ALIGN = 3,     /* a device pointer that is not 16-byte aligned */
+    W4A4_ERR_DEVICE = 4,    /* a HIP runtime error from a launch, copy or synchronisation */
+    W4A4_ERR_NONFINITE = 5  /* calibration data holds NaN or Inf */
+} w4a4_status;
+
+enum { W4A4_X_F32 = 0, W4A4_X_BF16 = 1 };
+
+/* Weight scale-group layouts (page above, sec. 3.4). */
+enum {
+    W4A4_WS_1X32 = 0,          /* B_s [d_out][K_pad/32]: one scale per row per 32 K          */
+    W4A4_WS_32X32_TILE = 1,    /* B_s [K_pad/32][ceil(d_out/32)]: 32 K x 32 rows per scale   */
+    W4A4_WS_128X1_STRIPE = 2   /* B_s [d_out][K_pad/128]: 128 K x 1 row, K-major stripes      */
+};
+
+/* Largest supported input width (act-prep stages one smoothed row, K_pad fp32,
+ * in LDS). */
+#define W4A4_MAX_D_IN 32768
+
+/* Packed layer descriptor, filled by w4a4_pack_weights.  Plain data: copy it
+ * freely; it points into the caller's blob and owns nothing. */
+typedef struct w4a4_packed {
+    int64_t d_in, d_out;
+    int32_t k;              /* |O|, number of BF16 outlier columns                        */
+    int32_t layout;         /* W4A4_WS_*                                                  */
+    int64_t k_j;            /* d_in - k                                                   */
+    int64_t k_pad;          /* roundup(k_j, 128)                                          */
+    int64_t k_ld;           /* row stride in elements of W_O and X_O: roundup(k, 32)      */
+    const int32_t* colmap;  /* device [d_in]: p >= 0 = J column at compacted position p;
+                               -(i+1) = outlier column O[i]                               */
+    const float* s;         /* device [d_in] smoothing factors                            */
+    const int32_t* O;       /* device [k], ascending                                      */
+    const int32_t* J;       /* device [k_j], ascending                                    */
+    const uint8_t* B_q;     /* device [d_out][k_pad/2] E2M1 codes of fl32(s_j * W[n][j])  */
+    const uint8_t* B_s;     /* device, E8M0 codes in the layout's shape (see enum)        */
+    const uint16_t* W_O;    /* device bf16 [d_out][k_ld], raw W[n][O[i]], zero padded     */
+} w4a4_packed;
+
+/* Offsets (bytes) of the quantized activations inside a workspace. */
+typedef struct w4a4_ws_layout {
+    size_t a_q;       /* uint8 [T][k_pad/2] activation E2M1 codes            */
+    size_t a_s;       /* uint8 [T][k_pad/32] activation E8M0 scales (1x32)    */
+    size_t x_o;       /* bf16  [T][k_ld] outlier columns, zero padded         */
+    size_t total;     /* bytes needed                                         */
+} w4a4_ws_layout;
+
+/* Human-readable name of a status code (static storage). */
+const char* w4a4_status_string(int status);
+
+/* Column-wise max |x| of a row-major [rows][cols] device matrix (fp32 or bf16),
+ * the per-channel magnitudes of sec. 3.2.  out_bits (device, [cols]) receives the
+ * binary32 bit pattern of each maximum; a pattern >= 0x7F800000 means the
+ * column holds NaN or Inf.  Async; out_bits is overwritten. */
+int w4a4_column_absmax(const void* X, int x_dtype, int64_t rows, int64_t cols,
+                       uint32_t* out_bits, void* stream);
+
+/* Offline calibration (sec. 3.2-3.3, order per sec. 2 / 3.5): per-channel maxima of
+ * X_cal (device [T_cal][d_in], fp32 or bf16) and of W (device fp32 [d_out][d_in],
+ * nn.Linear orientation, reduced over d_out), then on the host in double:
+ *   s_j = max(a_j,1e-5)^alpha / max(w_j,1e-5)^(1-alpha), rounded once to fp32,
+ *   score_j = fl32(a_j / s_j), O = top-k scores (ties -> smaller j), ascending.
+ * s_out [d_in] and O_out [k] are HOST buffers; act_scale_out / weight_scale_out
+ * (host [d_in]) may be NULL.  Blocking: synchronises `stream`.  Allocates a
+ * small device scratch (8*d_in bytes) internally.  Returns W4A4_ERR_NONFINITE if
+ * either input holds NaN/Inf. */
+int w4a4_calibrate_scales(const void* X_cal, int x_dtype, int64_t T_cal, int64_t d_in,
+                          const float* W, int64_t d_out, float alpha, int32_t k,
+                          float* s_out, int32_t* O_out,
+                          float* act_scale_out, float* weight_scale_out, void* stream);
+
+/* Bytes of the device blob that w4a4_pack_weights fills. */
+int w4a4_packed_size(int64_t d_in, int64_t d_out, int32_t k, int layout, size_t* bytes);
+
+/* Offline fold + split + pack (sec. 3.2 fold, 3.3 split, 3.4 block packing):
+ * W device fp32 [d_out][d_in]; s (host [d_in], s_j > 0 finite) and O (host [k],
+ * strictly ascending, in [0,d_in)) as produced by calibration (s = 1, k = 0 gives
+ * naive W4A4).  Writes B_q = E2M1(fl32(s_j * W[n][J[p]])) with E8M0 scales in
+ * `layout`, W_O = bf16_rne(W[n][O[i]]), plus s, O, J and the column map, into
+ * `blob` (device, blob_bytes >= w4a4_packed_size), and fills *desc.  Blocking:
+ * synchronises `stream` (host inputs are staged before return). */
+int w4a4_pack_weights(const float* W, int64_t d_in, int64_t d_out, const float* s,
+                      const int32_t* O, int32_t k, int layout, void* blob,
+                      size_t blob_bytes, w4a4_packed* desc, void* stream);
+
+/* Workspace offsets and size for T tokens with this layer. */
+int w4a4_workspace_layout(int64_t T, const w4a4_packed* desc, w4a4_ws_layout* out);
+int w4a4_workspace_size(int64_t T, const w4a4_packed* desc, size_t* bytes);
+
+/* Act-prep (sec. 3.2 "divide by s, then quantize", sec. 3.3 split): X device
+ * [T][d_in] fp32 or bf16, row-major contiguous.  For each token: x~ = fl32(x / s_j)
+ * (IEEE binary32 division, subnormals kept) over the J columns in ascending order,
+ * 1x32 E8M0 + E2M1 codes into A_q/A_s; X_O = bf16_rne(x) over the O columns.
+ * Async on `stream`; never allocates. */
+int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Dual-branch GEMM (sec. 3.3) on quantized activations already in `ws`:
+ * Y[t][n] = sum_b 2^(Ea+Eb) sum_{p in b} a.b  (block-scaled FP4 MFMA)
+ *         + sum_i X_O[t][i] W_O[n][i]         (BF16 MFMA, same fp32 accumulator)
+ * Y device fp32 [T][d_out].  Async; never allocates. */
+int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
+                           float* Y, void* stream);
+
+/* The per-call path: act-prep then the dual-branch GEMM.  Async; never allocates. */
+int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* GELU-tanh between the FFN up (ffn.0) and down (ffn.2) projections named in
+ * sec. 3.1 / 3.5: H = bf16_rne(gelu_tanh(bf16_rne(Y))), gelu_tanh(x) =
+ * 0.5x(1+tanh(sqrt(2/pi)(x+0.044715x^3))) in fp32.  Y device fp32 [n], H device
+ * bf16 [n].  Async. */
+int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

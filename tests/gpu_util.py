@@ -1,0 +1,110 @@
+"""Shared helpers of the GPU parity tests: device transfer and the output tolerance."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from bit_quantized_dit_amd import w4a4 as B
+
+# Output tolerance of the fp32 GEMM against the oracle's fp64 sum of the same codes:
+# max |dY| <= 1e-3 * max |Y_ref| and ||dY||_F / ||Y_ref||_F <= 1e-5.
+Y_MAX_REL = 1e-3
+Y_FRO_REL = 1e-5
+
+
+def to_dev(X: np.ndarray) -> torch.Tensor:
+    """numpy fp32, or bf16 bit patterns in uint16, -> device tensor of that dtype."""
+    if X.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32)).cuda()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().cpu().numpy().view(np.uint8)
+
+
+def assert_y_close(Y: np.ndarray, Yref: np.ndarray, what: str = "Y") -> dict:
+    Y = np.asarray(Y, dtype=np.float64)
+    Yref = np.asarray(Yref, dtype=np.float64)
+    nan_ref = np.isnan(Yref)
+    assert np.array_equal(np.isnan(Y), nan_ref), f"{what}: NaN pattern differs"
+    fin = ~nan_ref
+    d = np.abs(Y[fin] - Yref[fin])
+    scale = np.abs(Yref[fin]).max() if fin.any() else 0.0
+    max_rel = float(d.max() / scale) if d.size and scale > 0 else float(d.max() if d.size else 0.0)
+    nrm = np.linalg.norm(Yref[fin])
+    fro = float(np.linalg.norm(Y[fin] - Yref[fin]) / nrm) if nrm > 0 else float(np.linalg.norm(Y[fin]))
+    assert max_rel <= Y_MAX_REL, f"{what}: max|dY|/max|Y| = {max_rel:.3e}"
+    assert fro <= Y_FRO_REL, f"{what}: relative Frobenius error {fro:.3e}"
+    return {"max_rel": max_rel, "fro_rel": fro}
+
+
+def _banner(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _layer(orc, X, Xc, W, alpha, k, layout):
+    """Calibrate + pack + linear on the GPU; the oracle redoes each step on the same
+    inputs.  Returns a dict of both sides' results."""
+    Xd, Xcd, Wd = to_dev(X), to_dev(Xc), to_dev(W)
+    s, O, act, wsc = B.w4a4_calibrate_scales(Xcd, Wd, alpha, k)
+    s_o, O_o, J_o, act_o, wsc_o, _ = orc.calibrate(Xc, W, alpha, k)
+    assert np.array_equal(act, act_o) and np.array_equal(wsc, wsc_o)
+    ulp = np.abs(s.view(np.int32).astype(np.int64) - s_o.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, "s differs from the oracle by more than 1 ulp"
+    assert np.array_equal(O, O_o)
+    J = np.setdiff1d(np.arange(W.shape[1]), O).astype(np.int32)
+    packed = B.w4a4_pack_weights(Wd, s, O, layout)
+    T = X.shape[0]
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, W.shape[0], dtype=torch.float32, device="cuda")
+    B.w4a4_linear(Xd, packed, Y, ws)
+    torch.cuda.synchronize()
+    # downstream steps use the library's s on both sides
+    pk_o = orc.pack_weights(W, s, O, J, layout)
+    return {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y, "pk_o": pk_o, "T": T}
+
+
+def _check_packed(r):
+    v = r["packed"].views()
+    pk = r["pk_o"]
+    k = r["O"].size
+    assert np.array_equal(v["s"].cpu().numpy(), r["s"])
+    cm = v["colmap"].cpu().numpy()
+    assert np.array_equal(cm[r["J"]], np.arange(r["J"].size))
+    assert np.array_equal(cm[r["O"]], -(np.arange(k) + 1))
+    if r["packed"].k_pad:
+        assert np.array_equal(u8(v["B_q"]), pk["Bq"]), "B_q differs"
+        assert np.array_equal(u8(v["B_s"]), pk["Bs"]), "B_s differs"
+    if k:
+        wo = bf16_bits(v["W_O"])
+        assert np.array_equal(wo[:, :k], pk["WO"]), "W_O differs"
+        assert np.all(wo[:, k:] == 0)
+
+
+def _check_act(orc, r, X, rows=None):
+    v = B.workspace_views(r["ws"], r["T"], r["packed"])
+    Xs = X if rows is None else X[rows]
+    Aq_o, As_o, XO_o = orc.act_prep(Xs, r["s"], r["O"], r["J"])
+    sel = slice(None) if rows is None else torch.as_tensor(rows, device="cuda")
+    Aq, As = u8(v["A_q"][sel]), u8(v["A_s"][sel])
+    assert np.array_equal(As, As_o), "A_s differs"
+    assert np.array_equal(Aq, Aq_o), "A_q differs"
+    k = r["O"].size
+    if k:
+        xo = bf16_bits(v["X_O"][sel])
+        assert np.array_equal(xo[:, :k], XO_o), "X_O differs"
+        assert np.all(xo[:, k:] == 0)
+    return Aq_o, As_o, XO_o
+
+
+def _check_y_full(orc, r, X):
+    Aq_o, As_o, XO_o = _check_act(orc, r, X)
+    Yref = orc.output_full(Aq_o, As_o, XO_o, r["pk_o"])
+    return assert_y_close(r["Y"].cpu().numpy(), Yref)
+
+

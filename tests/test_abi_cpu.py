@@ -1,0 +1,116 @@
+"""The C-ABI library loads and exports every entry point the header declares; host-side
+validation and size queries behave as documented.  No call here reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_dit_amd import w4a4 as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "w4a4.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(w4a4_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from bit_quantized_dit_amd import build
+        build.build_library()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 11
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.w4a4_status_string(0) == b"ok"
+    assert b"invalid" in L.w4a4_status_string(1)
+    assert L.w4a4_status_string(99) == b"unknown status"
+
+
+def test_packed_size_layouts(L):
+    # d_in 512, k 16 -> K_J 496, K_pad 512; d_out 1024
+    s1 = B.w4a4_packed_size(512, 1024, 16, B.W4A4_WS_1X32)
+    s2 = B.w4a4_packed_size(512, 1024, 16, B.W4A4_WS_128X1_STRIPE)
+    s3 = B.w4a4_packed_size(512, 1024, 16, B.W4A4_WS_32X32_TILE)
+    payload = 1024 * 256
+    assert s1 >= payload + 1024 * 16 + 1024 * 32 * 2
+    assert s2 < s1 and s3 < s1
+    for s in (s1, s2, s3):
+        assert s % 256 == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((512, 1024, 16, 7), 1),        # bad layout
+    ((512, 1024, 513, 0), 1),       # k > d_in
+    ((512, 1024, -1, 0), 1),        # k < 0
+    ((0, 1024, 0, 0), 1),           # empty d_in
+    ((40000, 1024, 0, 0), 2),       # d_in beyond the supported maximum
+])
+def test_packed_size_rejects(L, args, code):
+    n = ctypes.c_size_t(0)
+    assert L.w4a4_packed_size(*args, ctypes.byref(n)) == code
+
+
+def _fake_desc(d_in=512, d_out=1024, k=16, layout=0):
+    d = B.W4A4Packed()
+    d.d_in, d.d_out, d.k, d.layout = d_in, d_out, k, layout
+    d.k_j = d_in - k
+    d.k_pad = (d.k_j + 127) // 128 * 128
+    d.k_ld = (k + 31) // 32 * 32
+    fake = 0x100000  # never dereferenced: only host-side logic runs below
+    d.colmap = d.s = d.O = d.J = d.B_q = d.B_s = d.W_O = fake
+    return d
+
+
+def test_workspace_layout_is_host_logic(L):
+    d = _fake_desc()
+    out = B.W4A4WsLayout()
+    assert L.w4a4_workspace_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 0
+    assert out.a_q == 0 and out.a_s >= 1000 * 256 and out.x_o >= out.a_s + 1000 * 16
+    assert out.total >= out.x_o + 1000 * 32 * 2 and out.total % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert L.w4a4_workspace_size(0, ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_per_call_entry_points_validate_before_any_launch(L):
+    d = _fake_desc()
+    n = ctypes.c_size_t(0)
+    # T < 0
+    assert L.w4a4_linear(ctypes.c_void_p(16), 0, -1, ctypes.byref(d), ctypes.c_void_p(16),
+                         ctypes.c_void_p(16), 1 << 30, None) == 1
+    # bad dtype
+    assert L.w4a4_quantize_activations(ctypes.c_void_p(16), 5, 4, ctypes.byref(d), ctypes.c_void_p(16),
+                                       1 << 30, None) == 1
+    # workspace too small
+    assert L.w4a4_quantize_activations(ctypes.c_void_p(256), 0, 4, ctypes.byref(d), ctypes.c_void_p(256),
+                                       10, None) == 2
+    # misaligned pointers
+    assert L.w4a4_gemm_prequantized(ctypes.c_void_p(258), 1 << 30, 4, ctypes.byref(d), ctypes.c_void_p(256),
+                                    None) == 3
+    # T == 0 is a no-op
+    assert L.w4a4_linear(None, 0, 0, ctypes.byref(d), None, None, 0, None) == 0
+    # inconsistent descriptor
+    bad = _fake_desc()
+    bad.k_pad = 128
+    assert L.w4a4_linear(ctypes.c_void_p(256), 0, 4, ctypes.byref(bad), ctypes.c_void_p(256),
+                         ctypes.c_void_p(256), 1 << 30, None) == 1
+    # calibration argument checks (alpha outside [0,1], k > d_in)
+    assert L.w4a4_calibrate_scales(ctypes.c_void_p(256), 0, 8, 64, ctypes.c_void_p(256), 32,
+                                   ctypes.c_float(1.5), 4, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   None, None, None) == 1
+    assert L.w4a4_calibrate_scales(ctypes.c_void_p(256), 0, 8, 64, ctypes.c_void_p(256), 32,
+                                   ctypes.c_float(0.5), 65, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   None, None, None) == 1
+    assert L.w4a4_gelu_tanh_bf16(ctypes.c_void_p(258), 8, ctypes.c_void_p(256), None) == 3

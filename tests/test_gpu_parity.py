@@ -1,0 +1,221 @@
+"""GPU parity of every step of the path against the CPU oracle, through the C ABI.
+
+Codes, scales, the column map, s and O must be bit-exact; Y must meet the output
+tolerance (tests/gpu_util.py).  Shapes span several 128x128 output tiles with ragged
+tails in T, d_out, K_J and k, both activation dtypes and all three weight layouts,
+plus the degenerate cases k = 0, k = d_in and special values.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_dit_amd import synth
+from bit_quantized_dit_amd import w4a4 as B
+from tests.gpu_util import (_banner, _check_act, _check_packed, _check_y_full, _layer,
+                            assert_y_close, bf16_bits, to_dev, u8)
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = [
+    # T, d_in, d_out, k, layout, dtype
+    (300, 704, 200, 13, 0, "bf16"),
+    (300, 700, 200, 13, 0, "f32"),      # d_in % 8 != 0: scalar load path
+    (257, 1000, 333, 40, 1, "bf16"),    # 32x32 tiles, ragged last tile
+    (129, 1536, 130, 64, 2, "f32"),     # 128x1 stripes
+    (64, 5120, 256, 128, 0, "bf16"),    # K_J = 4992: odd number of 128-steps
+    (1, 512, 64, 16, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,layout,dt", SMALL)
+def test_layer_parity(orc, T, d_in, d_out, k, layout, dt):
+    _banner(f"layer T={T} d_in={d_in} d_out={d_out} k={k} layout={layout} {dt}")
+    spec = synth.WORKLOADS[2 if dt == "bf16" else 1]
+    inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=97)
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, k, layout)
+    _check_packed(r)
+    _check_y_full(orc, r, inp["X"])
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2])
+def test_k0_naive_w4a4(orc, layout):
+    """k = 0 and s = 1: the plain MXFP4 GEMM (no outlier branch, no smoothing)."""
+    _banner(f"naive layout={layout}")
+    rng = np.random.default_rng(20 + layout)
+    T, d_in, d_out = 200, 384, 160
+    X = (rng.standard_normal((T, d_in)) * 0.5).astype(np.float32)
+    W = (rng.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)
+    s = np.ones(d_in, np.float32)
+    O = np.zeros(0, np.int32)
+    J = np.arange(d_in, dtype=np.int32)
+    packed = B.w4a4_pack_weights(to_dev(W), s, O, layout)
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, d_out, device="cuda")
+    B.w4a4_linear(to_dev(X), packed, Y, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y,
+         "pk_o": orc.pack_weights(W, s, O, J, layout), "T": T}
+    _check_packed(r)
+    _check_y_full(orc, r, X)
+
+
+def test_k_equals_din_pure_bf16(orc):
+    """k = d_in: J is empty, only the BF16 branch runs."""
+    _banner("k = d_in")
+    rng = np.random.default_rng(30)
+    T, d_in, d_out = 150, 96, 140
+    X = to_bits = synth.to_bf16_bits((rng.standard_normal((T, d_in))).astype(np.float32))
+    W = (rng.standard_normal((d_out, d_in)) * 0.1).astype(np.float32)
+    s = np.ones(d_in, np.float32)
+    O = np.arange(d_in, dtype=np.int32)
+    J = np.zeros(0, np.int32)
+    packed = B.w4a4_pack_weights(to_dev(W), s, O, 0)
+    assert packed.k_pad == 0
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, d_out, device="cuda")
+    B.w4a4_linear(to_dev(to_bits), packed, Y, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y,
+         "pk_o": orc.pack_weights(W, s, O, J, 0), "T": T}
+    _check_packed(r)
+    _check_y_full(orc, r, X)
+
+
+def test_special_values(orc):
+    """NaN/Inf rows give 0xFF blocks and NaN outputs; subnormals, -0, exact E2M1 ties
+    after division, and huge/tiny rows quantize bit-exactly."""
+    _banner("special values")
+    rng = np.random.default_rng(40)
+    T, d_in, d_out = 64, 256, 96
+    X = (rng.standard_normal((T, d_in)) * 0.3).astype(np.float32)
+    X[1, 5] = np.nan
+    X[2, 200] = np.inf
+    X[3, :] = np.float32(2.0 ** -140)           # subnormal-only row
+    X[4, :] = -0.0
+    X[5, ::3] = np.float32(2.0 ** -127)
+    X[6, :] *= np.float32(1e30)
+    X[7, :] = np.array([0x1], np.uint32).view(np.float32)[0]
+    X[8, :] = np.float32(3.0) * np.float32(2.5)  # divides to the tie 2.5 when s = 3
+    X[8, 0] = np.float32(21.0)
+    s = np.full(d_in, 3.0, np.float32)
+    s[::7] = np.float32(0.37)
+    W = (rng.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)
+    O = np.array([3, 77], np.int32)
+    J = np.setdiff1d(np.arange(d_in), O).astype(np.int32)
+    packed = B.w4a4_pack_weights(to_dev(W), s, O, 0)
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, d_out, device="cuda")
+    B.w4a4_linear(to_dev(X), packed, Y, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y,
+         "pk_o": orc.pack_weights(W, s, O, J, 0), "T": T}
+    Aq_o, As_o, XO_o = _check_act(orc, r, X)
+    assert (As_o == 0xFF).any()
+    Yref = orc.output_full(Aq_o, As_o, XO_o, r["pk_o"])
+    assert_y_close(Y.cpu().numpy(), Yref)
+
+
+def test_division_exhaustive_sample(orc):
+    """IEEE binary32 division on the GPU: 2^22 fp32 patterns spread over all exponents
+    (both signs) divided by assorted s, quantized in single-element-dominated blocks,
+    compared bit-exactly with the oracle."""
+    _banner("division sweep")
+    rng = np.random.default_rng(50)
+    pats = (np.arange(1 << 22, dtype=np.uint64) * 1021) % (1 << 32)
+    X = pats.astype(np.uint32).view(np.float32).reshape(-1, 256)
+    X = np.where(np.isfinite(X), X, np.float32(1.0)).astype(np.float32)
+    s = rng.uniform(0.01, 100, 256).astype(np.float32)
+    s[:8] = np.array([3.0, 1.0, 0.5, 7.0, 0x3FFD37D0, 1e-5, 1e5, 1.1], np.float32)
+    s[4] = np.array([0x3FFD37D0], np.uint32).view(np.float32)[0]
+    O = np.zeros(0, np.int32)
+    J = np.arange(256, dtype=np.int32)
+    W = np.ones((32, 256), np.float32) * 0.01
+    packed = B.w4a4_pack_weights(to_dev(W), s, O, 0)
+    T = X.shape[0]
+    ws = B.alloc_workspace(T, packed)
+    B.w4a4_quantize_activations(to_dev(X), packed, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "T": T}
+    _check_act(orc, r, X)
+
+
+def test_column_absmax_bits(orc):
+    rng = np.random.default_rng(60)
+    X = (rng.standard_normal((333, 1111)) * rng.uniform(0, 5, 1111)).astype(np.float32)
+    out = B.w4a4_column_absmax(to_dev(X))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float32)
+    assert np.array_equal(got, orc.col_absmax(X))
+    X[10, 7] = np.nan
+    out = B.w4a4_column_absmax(to_dev(X))
+    assert out.cpu().numpy().view(np.uint32)[7] >= 0x7F800000
+
+
+def test_calibration_rejects_nonfinite():
+    X = np.ones((16, 64), np.float32)
+    X[3, 3] = np.inf
+    W = np.ones((32, 64), np.float32)
+    with pytest.raises(B.W4A4Error) as e:
+        B.w4a4_calibrate_scales(to_dev(X), to_dev(W), 0.5, 4)
+    assert e.value.status == 5
+
+
+def test_determinism_and_prequantized_split(orc):
+    """Two runs are bitwise equal; act-prep + GEMM as separate calls equals w4a4_linear."""
+    spec = synth.WORKLOADS[2]
+    inp = synth.layer_inputs(spec, T=512, d_in=1024, d_out=384, k=32, T_cal=128)
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, 32, 0)
+    Xd = to_dev(inp["X"])
+    Y2 = torch.empty_like(r["Y"])
+    ws2 = torch.empty_like(r["ws"])
+    B.w4a4_quantize_activations(Xd, r["packed"], ws2)
+    B.w4a4_gemm_prequantized(ws2, r["T"], r["packed"], Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(r["Y"].view(torch.int32), Y2.view(torch.int32))
+    Y3 = torch.empty_like(r["Y"])
+    B.w4a4_linear(Xd, r["packed"], Y3, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(r["Y"].view(torch.int32), Y3.view(torch.int32))
+
+
+def test_error_paths_on_device():
+    W = torch.zeros(64, 128, device="cuda")
+    packed = B.w4a4_pack_weights(W, np.ones(128, np.float32), np.array([1, 2], np.int32), 0)
+    X = torch.zeros(10, 128, device="cuda")
+    Y = torch.empty(10, 64, device="cuda")
+    ws = B.alloc_workspace(10, packed)
+    with pytest.raises(B.W4A4Error) as e:
+        B.w4a4_linear(X, packed, Y, ws[:100])
+    assert e.value.status == 2
+    with pytest.raises(B.W4A4Error) as e:
+        B.w4a4_pack_weights(W, np.ones(128, np.float32), np.array([2, 1], np.int32), 0)
+    assert e.value.status == 1
+    with pytest.raises(B.W4A4Error) as e:
+        B.w4a4_pack_weights(W, -np.ones(128, np.float32), np.array([1], np.int32), 0)
+    assert e.value.status == 1
+    big = torch.empty(10 * 128 + 4, device="cuda")
+    with pytest.raises(B.W4A4Error) as e:
+        B.w4a4_linear(big[1:].view(10, 128), packed, Y, ws)
+    assert e.value.status == 3
+
+
+def test_gelu_kernel(orc, mini):
+    """GPU GELU-tanh in fp32 vs the oracle's double-precision formula: at most one bf16
+    ulp apart, and the mismatch count is small."""
+    rng = np.random.default_rng(70)
+    Yh = np.concatenate([rng.standard_normal(1 << 20) * 3, np.linspace(-12, 12, 4097)]).astype(np.float32)
+    H = torch.empty(Yh.size, dtype=torch.bfloat16, device="cuda")
+    B.w4a4_gelu_tanh_bf16(to_dev(Yh), H)
+    torch.cuda.synchronize()
+    got = bf16_bits(H)
+    ref = orc.gelu_bf16(Yh)
+    a = mini.bf16_to_f64(got)
+    b = mini.bf16_to_f64(ref)
+    big = np.abs(b) > 1e-6
+    ulp = np.abs(b[big]) * 2.0 ** -7
+    assert np.all(np.abs(a[big] - b[big]) <= ulp)
+    assert np.all(np.abs(a[~big]) <= 2e-6)
+    mism = int(np.sum(got != ref))
+    _banner(f"gelu mismatches: {mism} of {got.size}")
+    assert mism <= got.size // 200

@@ -1,0 +1,140 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (w4a4_linear on the whole token batch).
+
+Where the oracle cannot redo a whole workload in seconds, it recomputes sampled
+token rows of the activation codes and sampled outputs one by one; codes are compared
+bit-exactly, outputs with the GEMM tolerance.  The FFN block is checked stage by stage:
+up-projection, GELU (oracle applied to the GPU's Y_up), down act-prep (oracle applied
+to the GPU's H) and down output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_dit_amd import synth
+from bit_quantized_dit_amd import w4a4 as B
+from tests.gpu_util import (_banner, _check_act, _check_packed, _check_y_full, _layer,
+                            assert_y_close, bf16_bits, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_pairs(rng, T, N, n_pairs=4096, full_rows=(0,)):
+    ts = rng.integers(0, T, n_pairs)
+    ns = rng.integers(0, N, n_pairs)
+    for t in full_rows:
+        ts = np.concatenate([ts, np.full(N, t)])
+        ns = np.concatenate([ns, np.arange(N)])
+    return ts, ns
+
+
+def _check_sampled(orc, r, X, rng, n_rows=256):
+    T = r["T"]
+    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n_rows)]))
+    Aq_o, As_o, XO_o = _check_act(orc, r, X, rows)
+    N = r["pk_o"]["d_out"]
+    # outputs at sampled (row, feature) pairs; full rows for the first and last token
+    loc = np.arange(rows.size)
+    ts_l, ns = _sample_pairs(rng, rows.size, N, 4096, full_rows=(0, rows.size - 1))
+    Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts_l, ns)
+    Ysel = r["Y"][torch.as_tensor(rows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
+    return assert_y_close(Ysel.cpu().numpy(), Yref), loc
+
+
+def test_workload1_tiny_full(orc):
+    spec = synth.WORKLOADS[1]
+    _banner(f"workload {spec.name}")
+    inp = synth.layer_inputs(spec)
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, spec.k, spec.layout)
+    _check_packed(r)
+    st = _check_y_full(orc, r, inp["X"])
+    _banner(f"  {st}")
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_workload_4096_tokens(orc, wid):
+    spec = synth.WORKLOADS[wid]
+    _banner(f"workload {spec.name}")
+    inp = synth.layer_inputs(spec)
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, spec.k, spec.layout)
+    _check_packed(r)
+    # the oracle redoes act-prep for every token here (a few seconds)
+    Aq_o, As_o, XO_o = _check_act(orc, r, inp["X"])
+    rng = np.random.default_rng(wid)
+    ts, ns = _sample_pairs(rng, r["T"], spec.d_out, 8192, full_rows=(0, r["T"] - 1))
+    Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts, ns)
+    Ysel = r["Y"][torch.as_tensor(ts, device="cuda"), torch.as_tensor(ns, device="cuda")]
+    st = assert_y_close(Ysel.cpu().numpy(), Yref)
+    # the heavy columns drawn by the generator are the ones calibration selects
+    overlap = np.intersect1d(r["O"], inp["heavy"]).size
+    _banner(f"  {st}; heavy columns selected as O: {overlap}/{spec.k}")
+
+
+def test_workload4_57600_tokens(orc):
+    spec = synth.WORKLOADS[4]
+    _banner(f"workload {spec.name}")
+    inp = synth.layer_inputs(spec)
+    heavy_max = synth.bf16_bits_to_f32(inp["X"][:, inp["heavy"]]).__abs__().max(axis=0)
+    assert np.all(heavy_max > 6.0)     # every heavy column reaches max |x| > 6
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, spec.k, spec.layout)
+    _check_packed(r)
+    st, _ = _check_sampled(orc, r, inp["X"], np.random.default_rng(4))
+    _banner(f"  {st}")
+
+
+def test_workload5_ffn_block(orc, mini):
+    up, down = synth.FFN_BLOCK["up"], synth.FFN_BLOCK["down"]
+    _banner("workload ffn_block_T57600")
+    inp = synth.layer_inputs(up)
+    r_up = _layer(orc, inp["X"], inp["X_cal"], inp["W"], up.alpha, up.k, up.layout)
+    _check_packed(r_up)
+    rng = np.random.default_rng(5)
+    st_up, _ = _check_sampled(orc, r_up, inp["X"], rng)
+    _banner(f"  up: {st_up}")
+    T = r_up["T"]
+    # GELU stage: oracle GELU of the GPU's Y_up on sampled rows, <= 1 bf16 ulp
+    H = torch.empty(T, up.d_out, dtype=torch.bfloat16, device="cuda")
+    B.w4a4_gelu_tanh_bf16(r_up["Y"], H)
+    torch.cuda.synchronize()
+    rows = np.unique(rng.integers(0, T, 64))
+    trow = torch.as_tensor(rows, device="cuda")
+    Hg = bf16_bits(H[trow])
+    Ho = orc.gelu_bf16(r_up["Y"][trow].cpu().numpy()).reshape(Hg.shape)
+    a, b = mini.bf16_to_f64(Hg), mini.bf16_to_f64(Ho)
+    big = np.abs(b) > 1e-6
+    assert np.all(np.abs(a[big] - b[big]) <= np.abs(b[big]) * 2.0 ** -7)
+    mism = int(np.sum(Hg != Ho))
+    _banner(f"  gelu: {mism} of {Hg.size} sampled elements differ by one bf16 ulp")
+    assert mism <= Hg.size // 200
+    # down layer: calibrated on the bf16 GELU of the unquantized up projection of the
+    # calibration tokens; run on the GPU's H
+    del r_up["ws"]
+    Wd = synth.weights(down, stream=5)
+    Xc_down = synth.down_calibration(inp["X_cal"], inp["W"])
+    Wdd, Xcd = to_dev(Wd), to_dev(Xc_down)
+    s, O, _, _ = B.w4a4_calibrate_scales(Xcd, Wdd, down.alpha, down.k)
+    s_o, O_o, *_ = orc.calibrate(Xc_down, Wd, down.alpha, down.k)
+    assert np.abs(s.view(np.int32).astype(np.int64) - s_o.view(np.int32)).max() <= 1
+    assert np.array_equal(O, O_o)
+    J = np.setdiff1d(np.arange(down.d_in), O).astype(np.int32)
+    packed = B.w4a4_pack_weights(Wdd, s, O, down.layout)
+    del r_up["Y"]
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, down.d_out, dtype=torch.float32, device="cuda")
+    B.w4a4_linear(H, packed, Y, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y, "T": T,
+         "pk_o": orc.pack_weights(Wd, s, O, J, down.layout)}
+    _check_packed(r)
+    drows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 128)]))
+    Hs = bf16_bits(H[torch.as_tensor(drows, device="cuda")])
+    Aq_o, As_o, XO_o = orc.act_prep(Hs, s, O, J)
+    v = B.workspace_views(ws, T, packed)
+    dsel = torch.as_tensor(drows, device="cuda")
+    assert np.array_equal(v["A_s"][dsel].cpu().numpy(), As_o)
+    assert np.array_equal(v["A_q"][dsel].cpu().numpy(), Aq_o)
+    ts_l, ns = _sample_pairs(rng, drows.size, down.d_out, 4096, full_rows=(0,))
+    Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts_l, ns)
+    Ysel = Y[torch.as_tensor(drows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
+    st = assert_y_close(Ysel.cpu().numpy(), Yref)
+    _banner(f"  down: {st}")
