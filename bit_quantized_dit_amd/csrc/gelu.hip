@@ -2,6 +2,9 @@
 // named in "W4A4 Quantization for Inference on Wan2.2-I2V-A14B (ICME 2026
 // Challenge)", sec. 3.1 and 3.5:  H = bf16(gelu_tanh(bf16(Y))) with
 // gelu_tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) in fp32.
+// It is evaluated as x / (1 + exp(-2z)), z = sqrt(2/pi)(x + 0.044715 x^3): the same
+// function (0.5(1 + tanh z) is the logistic of 2z), but free of the cancellation in
+// 1 + tanh z that wipes out every digit of the negative tail in binary32.
 // Elementwise and HBM-bound: 8 elements per thread, 32-byte loads, 16-byte stores.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
@@ -11,8 +14,8 @@ namespace w4a4 {
 __device__ __forceinline__ uint16_t gelu_one(float y) {
     const float x = bf16_to_f32(bf16_rne(y));
     const float c = 0.7978845608028654f;   // sqrt(2/pi)
-    const float inner = c * (x + 0.044715f * x * x * x);
-    return bf16_rne(0.5f * x * (1.0f + tanhf(inner)));
+    const float z = c * (x + 0.044715f * x * x * x);
+    return bf16_rne(x / (1.0f + expf(-2.0f * z)));
 }
 
 __global__ __launch_bounds__(256) void gelu_kernel(const float* __restrict__ Y, int64_t n,

@@ -5,166 +5,355 @@
 //           + sum_i X_O[t][i] W_O[n][i]                         (BF16 x BF16)
 //
 // Both branches accumulate into the same fp32 registers:
-//   - the J branch with v_mfma_scale_f32_16x16x128_f8f6f4 in FP4 (E2M1) mode, whose
-//     per-lane E8M0 scale operand applies 2^(c-127) per 32-element K block to each
+//   - the J branch with v_mfma_scale_f32_32x32x64_f8f6f4 in FP4 (E2M1) mode, whose
+//     per-lane E8M0 scale operands apply 2^(c-127) per 32-element K block to each
 //     operand, i.e. exactly the MXFP4 block scaling;
-//   - the O branch with v_mfma_f32_16x16x32_bf16.
-// Operand roles: src0 = weight rows (16 features), src1 = activation rows (16
-// tokens), so each lane ends up holding 4 consecutive features of one token and
-// stores them as one float4.
+//   - the O branch with v_mfma_f32_32x32x16_bf16 (lane l feeds row l%32 and
+//     values 8(l/32)..8(l/32)+7 of a 16-wide step).
+// (The 32x32 shapes sustain close to the FP4 peak from a single wavefront per SIMD;
+// the 16x16x128 shape issues at about half that rate.)
+// Operand roles: src0 = weight rows (32 features), src1 = activation rows (32
+// tokens).  Lane l of a 32x32x64 operand feeds row l%32 and the 32-code K chunk l/32
+// (16 bytes, even K index in the low nibble) together with the E8M0 byte of that
+// chunk; lane l of the result holds token l%32 and features 8q + 4(l/32) + r, r < 4,
+// in registers 4q + r, stored as four float4.
 //
-// Tiling: a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 128-token x
-// 128-feature output tile; each wavefront a 64 x 64 sub-tile (4 x 4 MFMA tiles).
-// Per 128-K step the workgroup stages 128 rows x 64 bytes of A and of B in LDS
-// (16-byte chunks XOR-swizzled by row so that fragment reads are bank-conflict
-// free) plus one 32-bit word of four E8M0 codes per row; weight scales of the
-// tile and stripe layouts are expanded to that per-row word while staging.
+// Tiling: a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256-token x
+// 256-feature output tile; each wavefront a 128 x 128 sub-tile (4 x 4 MFMA tiles,
+// 256 fp32 accumulators per lane, held in AGPRs).  The K loop walks 128-code steps
+// (64 bytes per row).  Operands move HBM/L2 -> LDS with buffer_load ... lds (no
+// VGPR staging) into a ring of STAGES slots; STAGES-1 steps are in flight while the
+// MFMAs of the current step run.  Each slot holds 256 + 256 rows of 64 bytes plus one
+// 32-bit word of four E8M0 codes per row.  After the FP4 steps the same ring streams
+// the outlier branch: 32 bf16 values of X_O and W_O per row are again 64 bytes, so
+// each BF16 step has the slot layout of an FP4 step (without scales) and feeds
+// v_mfma_f32_32x32x16_bf16 into the same accumulators.
+// 16-byte chunks are XOR-swizzled by row
+// (the swizzle is applied to the global source address, since the DMA writes each
+// wavefront's 1 KiB contiguously) so that fragment reads are bank-conflict free.
+// Buffer descriptors cover exactly the tile's valid rows: rows past the token or
+// feature tail read as zero, with no masking in the loop.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with its
+// own L2.  The linear block id is remapped so that each XCD owns a contiguous range
+// of tiles, and tiles are ordered in groups of GROUP_M token panels so that the
+// workgroups resident on one XCD share A (token) and B (feature) panels in its L2.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
 
 namespace w4a4 {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int G_THREADS = 256;
-constexpr int BT = 128;          // tokens per workgroup tile
-constexpr int BF = 128;          // features per workgroup tile
-constexpr int FT = 4;            // 16-token MFMA tiles per wavefront
-constexpr int FF = 4;            // 16-feature MFMA tiles per wavefront
-constexpr int ROW_BYTES = 64;    // 128 FP4 codes per row per K step
+constexpr int BT = 256;                      // tokens per workgroup tile
+constexpr int BF = 256;                      // features per workgroup tile
+constexpr int FT = 4;                        // 32-token MFMA tiles per wavefront
+constexpr int FF = 4;                        // 32-feature MFMA tiles per wavefront
+constexpr int ROW_BYTES = 64;                // 128 FP4 codes per row per K step
+constexpr int A_OFF = 0;                     // slot layout: A codes | B codes | A scales | B scales
+constexpr int B_OFF = BT * ROW_BYTES;
+constexpr int AS_OFF = (BT + BF) * ROW_BYTES;
+constexpr int BS_OFF = AS_OFF + BT * 4;
+constexpr int SLOT_BYTES = BS_OFF + BF * 4;  // 34 KiB
+constexpr int STAGES = 4;
+constexpr int DMA_PER_STAGE = 10;            // per wavefront: 4 A + 4 B code chunks, 1 + 1 scale words
+constexpr int GROUP_M = 8;
+constexpr int NUM_XCD = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROW_BYTES + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-__device__ __forceinline__ uint32_t weight_scale_word(const uint8_t* __restrict__ Bs, int64_t n, int64_t kb,
-                                                      int64_t k_pad, int64_t N, int layout) {
-    if (layout == W4A4_WS_1X32) return *reinterpret_cast<const uint32_t*>(Bs + n * (k_pad / 32) + kb * 4);
-    if (layout == W4A4_WS_128X1_STRIPE) return 0x01010101u * (uint32_t)Bs[n * (k_pad / 128) + kb];
-    const int64_t ntile = (N + 31) / 32;
-    const int64_t base = (kb * 4) * ntile + n / 32;
-    return (uint32_t)Bs[base] | ((uint32_t)Bs[base + ntile] << 8) | ((uint32_t)Bs[base + 2 * ntile] << 16) |
-           ((uint32_t)Bs[base + 3 * ntile] << 24);
+// Raw buffer descriptor (gfx9 family): base, 16 high address bits, no stride,
+// num_records = byte range, word 3 = 32-bit data format.  Out-of-range loads read 0.
+__device__ __forceinline__ v4i make_srd(const void* p, uint32_t nbytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+    r[3] = 0x00020000;
+    return r;
 }
 
-__global__ __launch_bounds__(G_THREADS) void gemm_w4a4_kernel(
+// Global -> LDS without VGPRs: lane i's 16 (4) bytes land at LDS m0 + 16*i (4*i).
+// The compiler does not track these writes, so the kernel waits on vmcnt itself
+// before the barrier that publishes a slot.  The instruction has no register
+// results; its address operands are read at issue.  Descriptor, LDS base and
+// soffset are wave-uniform by construction; readfirstlane only tells the compiler.  One wait state separates the
+// SALU write of m0 from the DMA that reads it.
+__device__ __forceinline__ v4i uniform(v4i r) {
+    return v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+__device__ __forceinline__ void dma16(v4i srd, uint32_t lds, int voff, int soff) {
+    srd = uniform(srd);
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(srd), "s"(soff));
+}
+__device__ __forceinline__ void dma4(v4i srd, uint32_t lds, int voff, int soff) {
+    srd = uniform(srd);
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(srd), "s"(soff));
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * ROW_BYTES + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// Block id -> (token tile, feature tile): XCD-contiguous ranges, grouped order.
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t nt_m, int64_t nt_n, int64_t& tm, int64_t& tn) {
+    const int64_t total = nt_m * nt_n;
+    const int64_t q = total / NUM_XCD, r = total % NUM_XCD;
+    const int64_t x = bid % NUM_XCD, j = bid / NUM_XCD;
+    const int64_t id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const int64_t per_group = GROUP_M * nt_n;
+    const int64_t g = id / per_group;
+    const int64_t first_m = g * GROUP_M;
+    const int64_t gsize = nt_m - first_m < GROUP_M ? nt_m - first_m : GROUP_M;
+    const int64_t in_g = id % per_group;
+    tm = first_m + in_g % gsize;
+    tn = in_g / gsize;
+}
+
+__global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As, const uint16_t* __restrict__ XO,
-    int64_t T, const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs,
-    const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, int layout,
-    float* __restrict__ Y, int vec_store) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[BT * ROW_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[BF * ROW_BYTES];
-    __shared__ uint32_t sAs[BT];
-    __shared__ uint32_t sBs[BF];
+    int64_t T, const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs_rows,
+    const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, float* __restrict__ Y,
+    int vec_store) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * SLOT_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wt = wave & 1;     // token half of the tile
     const int wf = wave >> 1;    // feature half of the tile
-    const int64_t t0 = (int64_t)blockIdx.x * BT;
-    const int64_t f0 = (int64_t)blockIdx.y * BF;
-    const int l16 = lane & 15;
-    const int lc = lane >> 4;    // K chunk (32 codes) this lane feeds
+    const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
+    int64_t tm, tn;
+    tile_of(blockIdx.x, nt_m, nt_n, tm, tn);
+    const int64_t t0 = tm * BT;
+    const int64_t f0 = tn * BF;
+    const int l32 = lane & 31;
+    const int lh = lane >> 5;    // which 32-code half of a 64-code MFMA step this lane feeds
 
-    v4f acc[FF][FT];
+    v16f acc[FF][FT];
 #pragma unroll
     for (int i = 0; i < FF; ++i)
 #pragma unroll
-        for (int j = 0; j < FT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FT; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int64_t a_ld = k_pad / 2;
-    const int64_t nkb = k_pad / 128;
-    for (int64_t kb = 0; kb < nkb; ++kb) {
-        // ---- stage A and B codes: thread -> (row, 16-byte chunk)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = (tid >> 2) + 64 * h;
-            const int c = tid & 3;
-            const int64_t t = t0 + r;
-            uint4 va = make_uint4(0, 0, 0, 0);
-            if (t < T) va = *reinterpret_cast<const uint4*>(Aq + t * a_ld + kb * 64 + c * 16);
-            *reinterpret_cast<uint4*>(sA + swz(r, c)) = va;
-            const int64_t n = f0 + r;
-            uint4 vb = make_uint4(0, 0, 0, 0);
-            if (n < N) vb = *reinterpret_cast<const uint4*>(Bq + n * a_ld + kb * 64 + c * 16);
-            *reinterpret_cast<uint4*>(sB + swz(r, c)) = vb;
-        }
-        if (tid < BT) {
-            const int64_t t = t0 + tid;
-            sAs[tid] = t < T ? *reinterpret_cast<const uint32_t*>(As + t * (k_pad / 32) + kb * 4) : 0u;
-        } else {
-            const int r = tid - BT;
-            const int64_t n = f0 + r;
-            sBs[r] = n < N ? weight_scale_word(Bs, n, kb, k_pad, N, layout) : 0u;
-        }
-        __syncthreads();
+    const int64_t a_ld = k_pad / 2;      // bytes per row of A_q / B_q
+    const int64_t s_ld = k_pad / 32;     // bytes per row of A_s / B_s_rows
+    const int64_t o_ld = k_ld * 2;       // bytes per row of X_O / W_O
+    const int nkb = (int)(k_pad / 128);  // FP4 steps (128 codes = 64 bytes per row)
+    const int nbf = (int)(k_ld / 32);    // BF16 steps (32 values = 64 bytes per row)
+    const int nsteps = nkb + nbf;
 
-        // ---- fragments and MFMAs
-        v8i af[FT], bfr[FF];
-        int as_[FT], bs_[FF];
+    if (nsteps > 0) {
+        const int64_t rows_a = T - t0 < BT ? T - t0 : BT;
+        const int64_t rows_b = N - f0 < BF ? N - f0 : BF;
+        const v4i srdA = make_srd(Aq + t0 * a_ld, (uint32_t)(rows_a * a_ld));
+        const v4i srdB = make_srd(Bq + f0 * a_ld, (uint32_t)(rows_b * a_ld));
+        const v4i srdAs = make_srd(As + t0 * s_ld, (uint32_t)(rows_a * s_ld));
+        const v4i srdBs = make_srd(Bs_rows + f0 * s_ld, (uint32_t)(rows_b * s_ld));
+        const v4i srdXO = make_srd(XO + t0 * k_ld, (uint32_t)(rows_a * o_ld));
+        const v4i srdWO = make_srd(WO + f0 * k_ld, (uint32_t)(rows_b * o_ld));
+        const v4i srd0 = make_srd(Aq, 0u);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+        // per-lane source offsets of this wavefront's four 1 KiB row blocks: block b
+        // covers rows 16b..16b+15; lane -> row 16b + lane/4, physical chunk lane%4,
+        // logical chunk = physical ^ ((row >> 2) & 3); one set per row stride
+        int voff[4], voffo[4];
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
-            const int r = wt * 64 + j * 16 + l16;
-            const uint4 q = *reinterpret_cast<const uint4*>(sA + swz(r, lc));
-            af[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            as_[j] = (int)(sAs[r] >> (8 * lc));
+        for (int h = 0; h < 4; ++h) {
+            const int row = 16 * (wave * 4 + h) + (lane >> 2);
+            const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
+            voff[h] = row * (int)a_ld + chunk;
+            voffo[h] = row * (int)o_ld + chunk;
         }
+        const int vsc = (64 * wave + lane) * (int)s_ld;
+
+        // Step st of the ring: FP4 codes + scales for st < nkb, the 64-byte column
+        // slice (st - nkb) of X_O / W_O for BF16 steps, and a null descriptor past the
+        // end (zero range: the loads return zeros and touch no memory).  Every step
+        // issues exactly DMA_PER_STAGE loads per wavefront, so the outstanding count,
+        // and with it every wait below, is the same on every iteration.
+        struct Src {
+            v4i a, b, as, bs;
+            int so, ss, fp4;
+        };
+        // Word-by-word scalar selects (a select of whole descriptors is lowered to a
+        // table in scratch memory).
+        auto pick = [&](bool c1, v4i x, bool c2, v4i y) __attribute__((always_inline)) {
+            v4i r;
 #pragma unroll
-        for (int i = 0; i < FF; ++i) {
-            const int r = wf * 64 + i * 16 + l16;
-            const uint4 q = *reinterpret_cast<const uint4*>(sB + swz(r, lc));
-            bfr[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            bs_[i] = (int)(sBs[r] >> (8 * lc));
-        }
+            for (int w = 0; w < 4; ++w)
+                r[w] = __builtin_amdgcn_readfirstlane(c1 ? x[w] : (c2 ? y[w] : srd0[w]));
+            return r;
+        };
+        auto src_of = [&](int st) __attribute__((always_inline)) {
+            Src r;
+            const bool fp4 = st < nkb, bf = !fp4 && st < nsteps;
+            r.fp4 = fp4;
+            r.a = pick(fp4, srdA, bf, srdXO);
+            r.b = pick(fp4, srdB, bf, srdWO);
+            r.as = pick(fp4, srdAs, false, srd0);
+            r.bs = pick(fp4, srdBs, false, srd0);
+            r.so = fp4 ? st * 64 : (bf ? (st - nkb) * 64 : 0);
+            r.ss = fp4 ? st * 4 : 0;
+            return r;
+        };
+        auto dma_code = [&](const Src& r, uint32_t slot, int h, int which) __attribute__((always_inline)) {
+            const int vo = r.fp4 ? voff[h] : voffo[h];
+            if (which == 0) dma16(r.a, slot + A_OFF + (wave * 4 + h) * 1024, vo, r.so);
+            else dma16(r.b, slot + B_OFF + (wave * 4 + h) * 1024, vo, r.so);
+        };
+        auto issue = [&](int st) __attribute__((always_inline)) {
+            const Src r = src_of(st);
+            const uint32_t slot = lds0 + (uint32_t)((st % STAGES) * SLOT_BYTES);
 #pragma unroll
-        for (int i = 0; i < FF; ++i)
+            for (int h = 0; h < 4; ++h) dma_code(r, slot, h, 0);
 #pragma unroll
-            for (int j = 0; j < FT; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bfr[i], af[j], acc[i][j], 4, 4, 0, bs_[i], 0, as_[j]);
+            for (int h = 0; h < 4; ++h) dma_code(r, slot, h, 1);
+            dma4(r.as, slot + AS_OFF + wave * 256, vsc, r.ss);
+            dma4(r.bs, slot + BS_OFF + wave * 256, vsc, r.ss);
+        };
+
+        // fragments of one half-step (64 FP4 codes or 16 bf16 values per row): 4 weight
+        // + 4 activation operands of 16 bytes, at chunk 2h + lane/32 of the 64-byte row
+        struct Frags {
+            v4i b[FF], a[FT];          // 16 bytes per operand (32 FP4 codes or 8 bf16)
+            uint32_t bs[FF], as[FT];   // raw scale words; the lane's byte is selected at use
+        };
+        auto load_b = [&](Frags& f, int st, int h, int i) __attribute__((always_inline)) {
+            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
+            const int r = wf * 128 + i * 32 + l32;
+            const uint4 q = *reinterpret_cast<const uint4*>(slot + B_OFF + swz(r, 2 * h + lh));
+            f.b[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+            f.bs[i] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[r];
+        };
+        auto load_a = [&](Frags& f, int st, int h, int j) __attribute__((always_inline)) {
+            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
+            const int r = wt * 128 + j * 32 + l32;
+            const uint4 q = *reinterpret_cast<const uint4*>(slot + A_OFF + swz(r, 2 * h + lh));
+            f.a[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+            f.as[j] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[r];
+        };
+        auto load_half = [&](Frags& f, int st, int h, int o) __attribute__((always_inline)) {   // o-th of 8 operand reads
+            if (o < 4) load_b(f, st, h, o);
+            else load_a(f, st, h, o - 4);
+        };
+        // one MFMA of a half-step; sh selects the lane's E8M0 byte of the scale words
+        auto mma_fp4 = [&](const Frags& f, int h, int i, int j) __attribute__((always_inline)) {
+            const int sh = 8 * (2 * h + lh);
+            const v8i b = v8i{f.b[i][0], f.b[i][1], f.b[i][2], f.b[i][3], 0, 0, 0, 0};
+            const v8i a = v8i{f.a[j][0], f.a[j][1], f.a[j][2], f.a[j][3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                b, a, acc[i][j], 4, 4, 0, (int)(f.bs[i] >> sh), 0, (int)(f.as[j] >> sh));
+        };
+        auto mma_bf16 = [&](const Frags& f, int i, int j) __attribute__((always_inline)) {
+            const v8bf wb = __builtin_bit_cast(v8bf, f.b[i]);
+            const v8bf xa = __builtin_bit_cast(v8bf, f.a[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, xa, acc[i][j], 0, 0, 0);
+        };
+
+        // Pipeline.  MFMAs issue in order, so the LDS fragment reads and the DMA issue
+        // are interleaved one by one between the MFMAs of the other half-step, where
+        // they co-execute with the matrix pipe (sched_barrier pins the order):
+        //   half 0 of step st: 16 MFMAs on f0, interleaved with the 8 fragment reads of
+        //                      half 1 (f1);
+        //   sync:              wait for step st+1's DMA and for this wavefront's reads
+        //                      of slot st, then one barrier (slot st is free, slot st+1
+        //                      visible);
+        //   half 1 of step st: 16 MFMAs on f1, interleaved with the 8 reads of half 0
+        //                      of step st+1 (f0) and the 10 DMAs refilling slot st with
+        //                      step st+STAGES.
+        // At the sync point steps st+1..st+STAGES-1 are in flight; waiting for all but
+        // the last STAGES-2 of them (vmcnt 20) leaves step st+1 landed.  The FP4 steps
+        // run first, then the BF16 steps of the outlier branch on the same ring.
+        static_assert(STAGES == 4 && DMA_PER_STAGE == 10, "vmcnt immediates below assume 4 x 10");
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) issue(st);
+        asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
         __syncthreads();
+        Frags f0, f1;
+#pragma unroll
+        for (int o = 0; o < 8; ++o) load_half(f0, 0, 0, o);
+
+        auto sync_and_refill_setup = [&](int st) __attribute__((always_inline)) {
+            asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot st fully read
+            __syncthreads();
+        };
+        auto half1 = [&](int st, bool fp4) __attribute__((always_inline)) {
+            const Src r = src_of(st + STAGES);
+            const uint32_t slot = lds0 + (uint32_t)(((st + STAGES) % STAGES) * SLOT_BYTES);
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                if (fp4) mma_fp4(f1, 1, s & 3, s >> 2);
+                else mma_bf16(f1, s & 3, s >> 2);
+                if (s < 8) load_half(f0, st + 1, 0, s);
+                if (s >= 4 && s < 8) dma_code(r, slot, s - 4, 0);
+                if (s >= 8 && s < 12) dma_code(r, slot, s - 8, 1);
+                if (s == 12) dma4(r.as, slot + AS_OFF + wave * 256, vsc, r.ss);
+                if (s == 13) dma4(r.bs, slot + BS_OFF + wave * 256, vsc, r.ss);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        for (int st = 0; st < nkb; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                mma_fp4(f0, 0, s & 3, s >> 2);
+                if ((s & 1) == 0) load_half(f1, st, 1, s >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sync_and_refill_setup(st);
+            __builtin_amdgcn_sched_barrier(0);
+            half1(st, true);
+        }
+        for (int st = nkb; st < nsteps; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                mma_bf16(f0, s & 3, s >> 2);
+                if ((s & 1) == 0) load_half(f1, st, 1, s >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sync_and_refill_setup(st);
+            __builtin_amdgcn_sched_barrier(0);
+            half1(st, false);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // ---- outlier branch: bf16 x bf16 into the same accumulators
-    for (int64_t kk = 0; kk < k_ld; kk += 32) {
-        v8bf xa[FT], wb[FF];
-#pragma unroll
-        for (int j = 0; j < FT; ++j) {
-            const int64_t t = t0 + wt * 64 + j * 16 + l16;
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (t < T) q = *reinterpret_cast<const uint4*>(XO + t * k_ld + kk + 8 * lc);
-            xa[j] = __builtin_bit_cast(v8bf, q);
-        }
-#pragma unroll
-        for (int i = 0; i < FF; ++i) {
-            const int64_t n = f0 + wf * 64 + i * 16 + l16;
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (n < N) q = *reinterpret_cast<const uint4*>(WO + n * k_ld + kk + 8 * lc);
-            wb[i] = __builtin_bit_cast(v8bf, q);
-        }
-#pragma unroll
-        for (int i = 0; i < FF; ++i)
-#pragma unroll
-            for (int j = 0; j < FT; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], xa[j], acc[i][j], 0, 0, 0);
-    }
-
-    // ---- epilogue: lane holds features 4*lc..4*lc+3 of token l16 in each tile
+    // ---- epilogue: lane holds token l32 and features 8q + 4*lh + r of each tile
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-        const int64_t t = t0 + wt * 64 + j * 16 + l16;
+        const int64_t t = t0 + wt * 128 + j * 32 + l32;
         if (t >= T) continue;
 #pragma unroll
         for (int i = 0; i < FF; ++i) {
-            const int64_t n = f0 + wf * 64 + i * 16 + 4 * lc;
-            float* dst = Y + t * N + n;
-            if (vec_store && n + 3 < N) {
-                *reinterpret_cast<v4f*>(dst) = acc[i][j];
-            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < N) dst[r] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = f0 + wf * 128 + i * 32 + 8 * q + 4 * lh;
+                float* dst = Y + t * N + n;
+                const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]};
+                if (vec_store && n + 3 < N) {
+                    *reinterpret_cast<v4f*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) dst[r] = v[r];
+                }
             }
         }
     }
@@ -173,12 +362,13 @@ __global__ __launch_bounds__(G_THREADS) void gemm_w4a4_kernel(
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
                        const w4a4_packed& d, float* Y, hipStream_t st) {
     if (T <= 0 || d.d_out <= 0) return hipSuccess;
-    const int64_t gx = (T + BT - 1) / BT;
-    const int64_t gy = (d.d_out + BF - 1) / BF;
-    if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+    const int64_t tiles = ((T + BT - 1) / BT) * ((d.d_out + BF - 1) / BF);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // 32-bit buffer offsets: one tile's rows of codes must span < 2 GiB
+    if ((int64_t)BT * (d.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)Y & 15u) == 0);
-    gemm_w4a4_kernel<<<dim3((unsigned)gx, (unsigned)gy), G_THREADS, 0, st>>>(
-        Aq, As, XO, T, d.B_q, d.B_s, d.W_O, d.d_out, d.k_pad, d.k_ld, d.layout, Y, vec_store);
+    gemm_w4a4_kernel<<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
+        Aq, As, XO, T, d.B_q, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, Y, vec_store);
     return hipGetLastError();
 }
 

@@ -79,6 +79,20 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const float* __restrict
     *dst = make_uint4(words[0], words[1], words[2], words[3]);
 }
 
+// Per-row copy of the weight scales in 1x32 form (one code per row per 32-block),
+// derived from the tile or stripe codes; the GEMM streams this array so that its
+// K loop is the same for every layout.
+__global__ __launch_bounds__(256) void pack_row_scales_kernel(const uint8_t* __restrict__ Bs, int64_t d_out,
+                                                              int64_t k_pad, int layout,
+                                                              uint8_t* __restrict__ Bs_rows) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nkb = k_pad / 32;
+    if (g >= d_out * nkb) return;
+    const int64_t n = g / nkb, kb = g % nkb;
+    Bs_rows[g] = layout == W4A4_WS_128X1_STRIPE ? Bs[n * (k_pad / 128) + kb / 4]
+                                                : Bs[kb * ((d_out + 31) / 32) + n / 32];
+}
+
 // Outlier rows in bf16, raw (unsmoothed), zero padded to k_ld.
 __global__ __launch_bounds__(256) void pack_outliers_kernel(const float* __restrict__ W,
                                                             const int32_t* __restrict__ O, int64_t d_in,
@@ -106,6 +120,12 @@ hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st) {
             W, d.s, d.J, d.d_in, d.d_out, d.k_j, d.k_pad, d.layout, d.B_s, (uint8_t*)d.B_q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (d.layout != W4A4_WS_1X32) {
+            pack_row_scales_kernel<<<blocks_for(d.d_out * (d.k_pad / 32)), 256, 0, st>>>(
+                d.B_s, d.d_out, d.k_pad, d.layout, (uint8_t*)d.B_s_rows);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     if (d.k_ld > 0) {
         pack_outliers_kernel<<<blocks_for(d.d_out * d.k_ld), 256, 0, st>>>(W, d.O, d.d_in, d.d_out, d.k,

@@ -36,7 +36,7 @@ class W4A4Packed(ctypes.Structure):
                 ("layout", ctypes.c_int32), ("k_j", ctypes.c_int64), ("k_pad", ctypes.c_int64),
                 ("k_ld", ctypes.c_int64), ("colmap", ctypes.c_void_p), ("s", ctypes.c_void_p),
                 ("O", ctypes.c_void_p), ("J", ctypes.c_void_p), ("B_q", ctypes.c_void_p),
-                ("B_s", ctypes.c_void_p), ("W_O", ctypes.c_void_p)]
+                ("B_s", ctypes.c_void_p), ("B_s_rows", ctypes.c_void_p), ("W_O", ctypes.c_void_p)]
 
 
 class W4A4WsLayout(ctypes.Structure):
@@ -161,6 +161,8 @@ class PackedLayer:
             out["B_q"] = view(d.B_q, d.d_out * d.k_pad // 2, torch.uint8, (d.d_out, d.k_pad // 2))
             out["B_s"] = view(d.B_s, bs_shape[0] * bs_shape[1], torch.uint8, bs_shape)
             out["J"] = view(d.J, d.k_j * 4, torch.int32, (d.k_j,))
+            out["B_s_rows"] = view(d.B_s_rows, d.d_out * d.k_pad // 32, torch.uint8,
+                                   (d.d_out, d.k_pad // 32))
         if d.k:
             out["W_O"] = view(d.W_O, d.d_out * d.k_ld * 2, torch.bfloat16, (d.d_out, d.k_ld))
             out["O"] = view(d.O, d.k * 4, torch.int32, (d.k,))

@@ -85,6 +85,9 @@ typedef struct w4a4_packed {
     const int32_t* J;       /* device [k_j], ascending                                    */
     const uint8_t* B_q;     /* device [d_out][k_pad/2] E2M1 codes of fl32(s_j * W[n][j])  */
     const uint8_t* B_s;     /* device, E8M0 codes in the layout's shape (see enum)        */
+    const uint8_t* B_s_rows;/* device [d_out][k_pad/32]: the same codes expanded to one per
+                               row per 32-block (equals B_s for W4A4_WS_1X32; a derived
+                               copy for tiles and stripes that the GEMM streams)          */
     const uint16_t* W_O;    /* device bf16 [d_out][k_ld], raw W[n][O[i]], zero padded     */
 } w4a4_packed;
 

@@ -196,7 +196,7 @@ def test_error_paths_on_device():
     assert e.value.status == 1
     big = torch.empty(10 * 128 + 4, device="cuda")
     with pytest.raises(B.W4A4Error) as e:
-        B.w4a4_linear(big[1:].view(10, 128), packed, Y, ws)
+        B.w4a4_linear(big[1:1281].view(10, 128), packed, Y, ws)
     assert e.value.status == 3
 
 
@@ -216,6 +216,7 @@ def test_gelu_kernel(orc, mini):
     ulp = np.abs(b[big]) * 2.0 ** -7
     assert np.all(np.abs(a[big] - b[big]) <= ulp)
     assert np.all(np.abs(a[~big]) <= 2e-6)
-    mism = int(np.sum(got != ref))
-    _banner(f"gelu mismatches: {mism} of {got.size}")
-    assert mism <= got.size // 200
+    # below ~1e-6 the double formula itself cancels (1 + tanh z), so only smallness is checked
+    mism = int(np.sum(got[big] != ref[big]))
+    _banner(f"gelu mismatches: {mism} of {int(big.sum())}")
+    assert mism <= big.sum() // 1000
