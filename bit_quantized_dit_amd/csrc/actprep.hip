@@ -11,7 +11,8 @@
 //   phase 2  each thread takes 8 consecutive compacted positions (two 16-byte LDS
 //            reads); four lanes form one 32-block, their |x| maxima meet through
 //            two xor-shuffles, and every lane emits 8 nibbles as one 32-bit store
-//            (lane 0 of the four also stores the E8M0 byte).
+//            (lane 0 of the four also stores the E8M0 byte, into the step-major
+//            scale array [k_pad/128][T][4] that the GEMM streams contiguously).
 // HBM traffic is the algorithmic minimum: X read once, A_q/A_s/X_O written once.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
@@ -53,8 +54,10 @@ __device__ __forceinline__ void route(float x, int32_t m, float s, float* row, u
 }
 
 // Phase 2 for one token row held in LDS.
+// as_t points at this token's scale slot of step 0 in the step-major A_s
+// ([k_pad/128][T][4]); step kb's slot is as_t + kb * as_step.
 __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, uint8_t* aq_row,
-                                             uint8_t* as_row) {
+                                             uint8_t* as_t, int64_t as_step) {
     for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += AP_COLS_PER_PASS) {
         const float4 a = *reinterpret_cast<const float4*>(row + p0);
         const float4 b = *reinterpret_cast<const float4*>(row + p0 + 4);
@@ -77,7 +80,7 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
             for (int i = 0; i < 8; ++i) word |= e2m1_nibble(v[i], inv) << (4 * i);
         }
         *reinterpret_cast<uint32_t*>(aq_row + p0 / 2) = word;
-        if ((threadIdx.x & 3) == 0) as_row[p0 / 32] = (uint8_t)code;
+        if ((threadIdx.x & 3) == 0) as_t[(p0 / 128) * as_step + (p0 / 32) % 4] = (uint8_t)code;
     }
 }
 
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(AP_THREADS) void actprep_kernel(
         }
         for (int64_t i = k + threadIdx.x; i < k_ld; i += AP_THREADS) xo_row[i] = 0;
         __syncthreads();
-        quantize_row(row, k_pad, Aq + t * (k_pad / 2), As + t * (k_pad / 32));
+        quantize_row(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
         __syncthreads();
     }
 }

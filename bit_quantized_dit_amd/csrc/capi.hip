@@ -46,11 +46,7 @@ BlobLayout blob_layout(int64_t d_in, int64_t d_out, int32_t k, int layout) {
     b.J = off;      off = align_up(off + (size_t)k_j * 4);
     b.B_q = off;    off = align_up(off + (size_t)(d_out * (k_pad / 2)));
     b.B_s = off;    off = align_up(off + (size_t)weight_scale_bytes(d_out, k_pad, layout));
-    b.B_s_rows = b.B_s;   // the 1x32 layout already is the per-row form
-    if (layout != W4A4_WS_1X32) {
-        b.B_s_rows = off;
-        off = align_up(off + (size_t)(d_out * (k_pad / 32)));
-    }
+    b.B_s_rows = off;     off = align_up(off + (size_t)(d_out * (k_pad / 32)));
     b.W_O = off;    off = align_up(off + (size_t)(d_out * k_ld) * 2);
     b.total = off;
     return b;

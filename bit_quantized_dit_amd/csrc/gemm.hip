@@ -18,13 +18,17 @@
 // chunk; lane l of the result holds token l%32 and features 8q + 4(l/32) + r, r < 4,
 // in registers 4q + r, stored as four float4.
 //
-// Tiling: a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256-token x
-// 256-feature output tile; each wavefront a 128 x 128 sub-tile (4 x 4 MFMA tiles,
-// 256 fp32 accumulators per lane, held in AGPRs).  The K loop walks 128-code steps
+// Tiling: a 512-thread workgroup (8 wavefronts, 2 token halves x 4 feature quarters,
+// two per SIMD) owns a 256-token x 256-feature output tile; each wavefront a
+// 128 x 64 sub-tile (4 x 2 MFMA tiles, 128 fp32 accumulators per lane in AGPRs), so
+// that one wavefront's LDS waits, barrier waits and epilogue stores are covered by
+// the MFMAs of its SIMD partner.  The 256 x 256 tile keeps the global traffic per
+// MFMA at the level that the per-CU vector memory path sustains.  The K loop walks 128-code steps
 // (64 bytes per row).  Operands move HBM/L2 -> LDS with buffer_load ... lds (no
 // VGPR staging) into a ring of STAGES slots; STAGES-1 steps are in flight while the
 // MFMAs of the current step run.  Each slot holds 256 + 256 rows of 64 bytes plus one
-// 32-bit word of four E8M0 codes per row.  After the FP4 steps the same ring streams
+// 32-bit word of four E8M0 codes per row (read from the step-major scale arrays, so
+// that one wavefront's 64 words are one contiguous 256-byte request).  After the FP4 steps the same ring streams
 // the outlier branch: 32 bf16 values of X_O and W_O per row are again 64 bytes, so
 // each BF16 step has the slot layout of an FP4 step (without scales) and feeds
 // v_mfma_f32_32x32x16_bf16 into the same accumulators.
@@ -49,11 +53,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int G_THREADS = 256;
+constexpr int G_THREADS = 512;               // 8 wavefronts: 2 per SIMD
 constexpr int BT = 256;                      // tokens per workgroup tile
 constexpr int BF = 256;                      // features per workgroup tile
-constexpr int FT = 4;                        // 32-token MFMA tiles per wavefront
-constexpr int FF = 4;                        // 32-feature MFMA tiles per wavefront
+constexpr int FT = 4;                        // 32-token MFMA tiles per wavefront (128 tokens)
+constexpr int FF = 2;                        // 32-feature MFMA tiles per wavefront (64 features)
 constexpr int ROW_BYTES = 64;                // 128 FP4 codes per row per K step
 constexpr int A_OFF = 0;                     // slot layout: A codes | B codes | A scales | B scales
 constexpr int B_OFF = BT * ROW_BYTES;
@@ -61,7 +65,7 @@ constexpr int AS_OFF = (BT + BF) * ROW_BYTES;
 constexpr int BS_OFF = AS_OFF + BT * 4;
 constexpr int SLOT_BYTES = BS_OFF + BF * 4;  // 34 KiB
 constexpr int STAGES = 4;
-constexpr int DMA_PER_STAGE = 10;            // per wavefront: 4 A + 4 B code chunks, 1 + 1 scale words
+constexpr int DMA_PER_STAGE = 5;             // per wavefront: 2 A + 2 B 1-KiB code blocks, 1 scale block
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
 
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wt = wave & 1;     // token half of the tile
-    const int wf = wave >> 1;    // feature half of the tile
+    const int wf = wave >> 1;    // feature quarter of the tile
     const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
     int64_t tm, tn;
     tile_of(blockIdx.x, nt_m, nt_n, tm, tn);
@@ -150,7 +154,6 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int64_t a_ld = k_pad / 2;      // bytes per row of A_q / B_q
-    const int64_t s_ld = k_pad / 32;     // bytes per row of A_s / B_s_rows
     const int64_t o_ld = k_ld * 2;       // bytes per row of X_O / W_O
     const int nkb = (int)(k_pad / 128);  // FP4 steps (128 codes = 64 bytes per row)
     const int nbf = (int)(k_ld / 32);    // BF16 steps (32 values = 64 bytes per row)
@@ -161,8 +164,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         const int64_t rows_b = N - f0 < BF ? N - f0 : BF;
         const v4i srdA = make_srd(Aq + t0 * a_ld, (uint32_t)(rows_a * a_ld));
         const v4i srdB = make_srd(Bq + f0 * a_ld, (uint32_t)(rows_b * a_ld));
-        const v4i srdAs = make_srd(As + t0 * s_ld, (uint32_t)(rows_a * s_ld));
-        const v4i srdBs = make_srd(Bs_rows + f0 * s_ld, (uint32_t)(rows_b * s_ld));
+        // Step-major scales: step st's words of this tile's rows start at
+        // (st * rows_total + row0) * 4.  The step offset goes into the descriptor base
+        // (not soffset, which the range check does not cover), so the descriptor spans
+        // exactly the tile's valid rows and tail rows read zero.
+        auto scale_srd = [&](const uint8_t* base, int st, int64_t total, int64_t row0, int64_t rows)
+            __attribute__((always_inline)) {
+            return make_srd(base + ((int64_t)st * total + row0) * 4, (uint32_t)(rows * 4));
+        };
         const v4i srdXO = make_srd(XO + t0 * k_ld, (uint32_t)(rows_a * o_ld));
         const v4i srdWO = make_srd(WO + f0 * k_ld, (uint32_t)(rows_b * o_ld));
         const v4i srd0 = make_srd(Aq, 0u);
@@ -170,15 +179,17 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         // per-lane source offsets of this wavefront's four 1 KiB row blocks: block b
         // covers rows 16b..16b+15; lane -> row 16b + lane/4, physical chunk lane%4,
         // logical chunk = physical ^ ((row >> 2) & 3); one set per row stride
-        int voff[4], voffo[4];
+        int voff[2], voffo[2];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int row = 16 * (wave * 4 + h) + (lane >> 2);
+        for (int h = 0; h < 2; ++h) {
+            const int row = 16 * (wave * 2 + h) + (lane >> 2);
             const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
             voff[h] = row * (int)a_ld + chunk;
             voffo[h] = row * (int)o_ld + chunk;
         }
-        const int vsc = (64 * wave + lane) * (int)s_ld;
+        // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words
+        const bool sc_b = wave >= 4;
+        const int vsc = (64 * (wave & 3) + lane) * 4;
 
         // Step st of the ring: FP4 codes + scales for st < nkb, the 64-byte column
         // slice (st - nkb) of X_O / W_O for BF16 steps, and a null descriptor past the
@@ -204,59 +215,66 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             r.fp4 = fp4;
             r.a = pick(fp4, srdA, bf, srdXO);
             r.b = pick(fp4, srdB, bf, srdWO);
-            r.as = pick(fp4, srdAs, false, srd0);
-            r.bs = pick(fp4, srdBs, false, srd0);
+            r.as = pick(fp4, scale_srd(As, fp4 ? st : 0, T, t0, rows_a), false, srd0);
+            r.bs = pick(fp4, scale_srd(Bs_rows, fp4 ? st : 0, N, f0, rows_b), false, srd0);
             r.so = fp4 ? st * 64 : (bf ? (st - nkb) * 64 : 0);
-            r.ss = fp4 ? st * 4 : 0;
+            r.ss = 0;
             return r;
         };
         auto dma_code = [&](const Src& r, uint32_t slot, int h, int which) __attribute__((always_inline)) {
             const int vo = r.fp4 ? voff[h] : voffo[h];
-            if (which == 0) dma16(r.a, slot + A_OFF + (wave * 4 + h) * 1024, vo, r.so);
-            else dma16(r.b, slot + B_OFF + (wave * 4 + h) * 1024, vo, r.so);
+            if (which == 0) dma16(r.a, slot + A_OFF + (wave * 2 + h) * 1024, vo, r.so);
+            else dma16(r.b, slot + B_OFF + (wave * 2 + h) * 1024, vo, r.so);
+        };
+        auto dma_scale = [&](const Src& r, uint32_t slot) __attribute__((always_inline)) {
+            dma4(sc_b ? r.bs : r.as, slot + (sc_b ? BS_OFF : AS_OFF) + (wave & 3) * 256, vsc, r.ss);
         };
         auto issue = [&](int st) __attribute__((always_inline)) {
             const Src r = src_of(st);
             const uint32_t slot = lds0 + (uint32_t)((st % STAGES) * SLOT_BYTES);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) dma_code(r, slot, h, 0);
+            for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 0);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) dma_code(r, slot, h, 1);
-            dma4(r.as, slot + AS_OFF + wave * 256, vsc, r.ss);
-            dma4(r.bs, slot + BS_OFF + wave * 256, vsc, r.ss);
+            for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 1);
+            dma_scale(r, slot);
         };
 
         // fragments of one half-step (64 FP4 codes or 16 bf16 values per row): 4 weight
         // + 4 activation operands of 16 bytes, at chunk 2h + lane/32 of the 64-byte row
         struct Frags {
             v4i b[FF], a[FT];          // 16 bytes per operand (32 FP4 codes or 8 bf16)
-            uint32_t bs[FF], as[FT];   // raw scale words; the lane's byte is selected at use
+        };
+        struct Scales {
+            uint32_t b[FF], a[FT];     // raw scale words of a step; the lane's byte is selected at use
         };
         auto load_b = [&](Frags& f, int st, int h, int i) __attribute__((always_inline)) {
             const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
-            const int r = wf * 128 + i * 32 + l32;
+            const int r = wf * 64 + i * 32 + l32;
             const uint4 q = *reinterpret_cast<const uint4*>(slot + B_OFF + swz(r, 2 * h + lh));
             f.b[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-            f.bs[i] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[r];
         };
         auto load_a = [&](Frags& f, int st, int h, int j) __attribute__((always_inline)) {
             const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
             const int r = wt * 128 + j * 32 + l32;
             const uint4 q = *reinterpret_cast<const uint4*>(slot + A_OFF + swz(r, 2 * h + lh));
             f.a[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-            f.as[j] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[r];
         };
-        auto load_half = [&](Frags& f, int st, int h, int o) __attribute__((always_inline)) {   // o-th of 8 operand reads
-            if (o < 4) load_b(f, st, h, o);
-            else load_a(f, st, h, o - 4);
+        auto load_scale = [&](Scales& c, int st, int o) __attribute__((always_inline)) {   // o-th of 6 words
+            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
+            if (o < FF) c.b[o] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[wf * 64 + o * 32 + l32];
+            else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * 128 + (o - FF) * 32 + l32];
+        };
+        auto load_half = [&](Frags& f, int st, int h, int o) __attribute__((always_inline)) {   // o-th of 6 operand reads
+            if (o < FF) load_b(f, st, h, o);
+            else load_a(f, st, h, o - FF);
         };
         // one MFMA of a half-step; sh selects the lane's E8M0 byte of the scale words
-        auto mma_fp4 = [&](const Frags& f, int h, int i, int j) __attribute__((always_inline)) {
+        auto mma_fp4 = [&](const Frags& f, const Scales& c, int h, int i, int j) __attribute__((always_inline)) {
             const int sh = 8 * (2 * h + lh);
             const v8i b = v8i{f.b[i][0], f.b[i][1], f.b[i][2], f.b[i][3], 0, 0, 0, 0};
             const v8i a = v8i{f.a[j][0], f.a[j][1], f.a[j][2], f.a[j][3], 0, 0, 0, 0};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                b, a, acc[i][j], 4, 4, 0, (int)(f.bs[i] >> sh), 0, (int)(f.as[j] >> sh));
+                b, a, acc[i][j], 4, 4, 0, (int)(c.b[i] >> sh), 0, (int)(c.a[j] >> sh));
         };
         auto mma_bf16 = [&](const Frags& f, int i, int j) __attribute__((always_inline)) {
             const v8bf wb = __builtin_bit_cast(v8bf, f.b[i]);
@@ -278,17 +296,22 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         // At the sync point steps st+1..st+STAGES-1 are in flight; waiting for all but
         // the last STAGES-2 of them (vmcnt 20) leaves step st+1 landed.  The FP4 steps
         // run first, then the BF16 steps of the outlier branch on the same ring.
-        static_assert(STAGES == 4 && DMA_PER_STAGE == 10, "vmcnt immediates below assume 4 x 10");
+        static_assert(STAGES == 4 && DMA_PER_STAGE == 5, "vmcnt immediates below assume 4 x 5");
 #pragma unroll
         for (int st = 0; st < STAGES; ++st) issue(st);
-        asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
         __syncthreads();
         Frags f0, f1;
+        Scales c0, c1;                 // scale words of the current and of the next step
 #pragma unroll
-        for (int o = 0; o < 8; ++o) load_half(f0, 0, 0, o);
+        for (int o = 0; o < FF + FT; ++o) {
+            load_half(f0, 0, 0, o);
+            load_scale(c0, 0, o);
+        }
 
+        constexpr int NM = FF * FT;   // MFMAs per half-step
         auto sync_and_refill_setup = [&](int st) __attribute__((always_inline)) {
-            asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot st fully read
             __syncthreads();
         };
@@ -296,35 +319,59 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             const Src r = src_of(st + STAGES);
             const uint32_t slot = lds0 + (uint32_t)(((st + STAGES) % STAGES) * SLOT_BYTES);
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                if (fp4) mma_fp4(f1, 1, s & 3, s >> 2);
-                else mma_bf16(f1, s & 3, s >> 2);
-                if (s < 8) load_half(f0, st + 1, 0, s);
-                if (s >= 4 && s < 8) dma_code(r, slot, s - 4, 0);
-                if (s >= 8 && s < 12) dma_code(r, slot, s - 8, 1);
-                if (s == 12) dma4(r.as, slot + AS_OFF + wave * 256, vsc, r.ss);
-                if (s == 13) dma4(r.bs, slot + BS_OFF + wave * 256, vsc, r.ss);
+            for (int s = 0; s < NM; ++s) {
+                if (fp4) mma_fp4(f1, c0, 1, s % FF, s / FF);
+                else mma_bf16(f1, s % FF, s / FF);
+                if (s < FF + FT) {
+                    load_half(f0, st + 1, 0, s);
+                    load_scale(c1, st + 1, s);
+                }
+                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0);
+                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1);
+                if (s == 5) dma_scale(r, slot);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        for (int st = 0; st < nkb; ++st) {
+        // FP4 steps, unrolled by two so that the scale words of the current and the
+        // next step alternate between c0 and c1 without a copy (a copy would wait for
+        // every outstanding LDS read at the end of each step)
+        auto fp4_step = [&](int st, Scales& cur, Scales& nxt) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                mma_fp4(f0, 0, s & 3, s >> 2);
-                if ((s & 1) == 0) load_half(f1, st, 1, s >> 1);
+            for (int s = 0; s < NM; ++s) {
+                mma_fp4(f0, cur, 0, s % FF, s / FF);
+                if (s < FF + FT) load_half(f1, st, 1, s);
                 __builtin_amdgcn_sched_barrier(0);
             }
             sync_and_refill_setup(st);
             __builtin_amdgcn_sched_barrier(0);
-            half1(st, true);
+            const Src r = src_of(st + STAGES);
+            const uint32_t slot = lds0 + (uint32_t)(((st + STAGES) % STAGES) * SLOT_BYTES);
+#pragma unroll
+            for (int s = 0; s < NM; ++s) {
+                mma_fp4(f1, cur, 1, s % FF, s / FF);
+                if (s < FF + FT) {
+                    load_half(f0, st + 1, 0, s);
+                    load_scale(nxt, st + 1, s);
+                }
+                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0);
+                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1);
+                if (s == 5) dma_scale(r, slot);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int st = 0;
+        for (; st + 1 < nkb; st += 2) {
+            fp4_step(st, c0, c1);
+            fp4_step(st + 1, c1, c0);
         }
-        for (int st = nkb; st < nsteps; ++st) {
+        if (st < nkb) fp4_step(st, c0, c1);
+        for (st = nkb; st < nsteps; ++st) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                mma_bf16(f0, s & 3, s >> 2);
-                if ((s & 1) == 0) load_half(f1, st, 1, s >> 1);
+            for (int s = 0; s < NM; ++s) {
+                mma_bf16(f0, s % FF, s / FF);
+                if (s < FF + FT) load_half(f1, st, 1, s);
                 __builtin_amdgcn_sched_barrier(0);
             }
             sync_and_refill_setup(st);
@@ -343,7 +390,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         for (int i = 0; i < FF; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = f0 + wf * 128 + i * 32 + 8 * q + 4 * lh;
+                const int64_t n = f0 + wf * 64 + i * 32 + 8 * q + 4 * lh;
                 float* dst = Y + t * N + n;
                 const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                   acc[i][j][4 * q + 3]};

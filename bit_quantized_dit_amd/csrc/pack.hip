@@ -79,9 +79,10 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const float* __restrict
     *dst = make_uint4(words[0], words[1], words[2], words[3]);
 }
 
-// Per-row copy of the weight scales in 1x32 form (one code per row per 32-block),
-// derived from the tile or stripe codes; the GEMM streams this array so that its
-// K loop is the same for every layout.
+// Step-major per-row copy of the weight scales: for each 128-code step kb, row n's
+// four 32-block codes at Bs_rows[(kb*d_out + n)*4 + q], derived from the canonical
+// codes of any layout.  One GEMM workgroup then reads a step's scales for its 256
+// rows as one contiguous 1 KiB run instead of 256 scattered words.
 __global__ __launch_bounds__(256) void pack_row_scales_kernel(const uint8_t* __restrict__ Bs, int64_t d_out,
                                                               int64_t k_pad, int layout,
                                                               uint8_t* __restrict__ Bs_rows) {
@@ -89,8 +90,11 @@ __global__ __launch_bounds__(256) void pack_row_scales_kernel(const uint8_t* __r
     const int64_t nkb = k_pad / 32;
     if (g >= d_out * nkb) return;
     const int64_t n = g / nkb, kb = g % nkb;
-    Bs_rows[g] = layout == W4A4_WS_128X1_STRIPE ? Bs[n * (k_pad / 128) + kb / 4]
-                                                : Bs[kb * ((d_out + 31) / 32) + n / 32];
+    uint8_t c;
+    if (layout == W4A4_WS_1X32) c = Bs[n * nkb + kb];
+    else if (layout == W4A4_WS_128X1_STRIPE) c = Bs[n * (k_pad / 128) + kb / 4];
+    else c = Bs[kb * ((d_out + 31) / 32) + n / 32];
+    Bs_rows[((kb / 4) * d_out + n) * 4 + (kb % 4)] = c;
 }
 
 // Outlier rows in bf16, raw (unsmoothed), zero padded to k_ld.
@@ -120,12 +124,10 @@ hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st) {
             W, d.s, d.J, d.d_in, d.d_out, d.k_j, d.k_pad, d.layout, d.B_s, (uint8_t*)d.B_q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (d.layout != W4A4_WS_1X32) {
-            pack_row_scales_kernel<<<blocks_for(d.d_out * (d.k_pad / 32)), 256, 0, st>>>(
-                d.B_s, d.d_out, d.k_pad, d.layout, (uint8_t*)d.B_s_rows);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+        pack_row_scales_kernel<<<blocks_for(d.d_out * (d.k_pad / 32)), 256, 0, st>>>(
+            d.B_s, d.d_out, d.k_pad, d.layout, (uint8_t*)d.B_s_rows);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     if (d.k_ld > 0) {
         pack_outliers_kernel<<<blocks_for(d.d_out * d.k_ld), 256, 0, st>>>(W, d.O, d.d_in, d.d_out, d.k,

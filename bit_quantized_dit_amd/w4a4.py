@@ -161,8 +161,10 @@ class PackedLayer:
             out["B_q"] = view(d.B_q, d.d_out * d.k_pad // 2, torch.uint8, (d.d_out, d.k_pad // 2))
             out["B_s"] = view(d.B_s, bs_shape[0] * bs_shape[1], torch.uint8, bs_shape)
             out["J"] = view(d.J, d.k_j * 4, torch.int32, (d.k_j,))
-            out["B_s_rows"] = view(d.B_s_rows, d.d_out * d.k_pad // 32, torch.uint8,
-                                   (d.d_out, d.k_pad // 32))
+            # step-major [k_pad/128][d_out][4] (raw) and the same codes as [d_out][k_pad/32]
+            raw = view(d.B_s_rows, d.d_out * d.k_pad // 32, torch.uint8, (d.k_pad // 128, d.d_out, 4))
+            out["B_s_rows_raw"] = raw
+            out["B_s_rows"] = raw.permute(1, 0, 2).reshape(d.d_out, d.k_pad // 32)
         if d.k:
             out["W_O"] = view(d.W_O, d.d_out * d.k_ld * 2, torch.bfloat16, (d.d_out, d.k_ld))
             out["O"] = view(d.O, d.k * 4, torch.int32, (d.k,))
@@ -246,11 +248,15 @@ def alloc_workspace(T: int, packed: PackedLayer, device="cuda") -> torch.Tensor:
 
 
 def workspace_views(ws: torch.Tensor, T: int, packed: PackedLayer) -> dict:
-    """Device views of A_q [T, k_pad/2], A_s [T, k_pad/32] and X_O [T, k_ld] inside ws."""
+    """Device tensors of the quantized activations inside ws: A_q [T, k_pad/2],
+    X_O [T, k_ld], A_s_raw (the step-major [k_pad/128, T, 4] array) and A_s (the same
+    codes as a [T, k_pad/32] copy)."""
     L = w4a4_workspace_layout(T, packed)
     kp, kl = packed.k_pad, packed.k_ld
+    raw = ws[L.a_s:L.a_s + T * kp // 32].view(kp // 128, T, 4)
     return {"A_q": ws[L.a_q:L.a_q + T * kp // 2].view(T, kp // 2),
-            "A_s": ws[L.a_s:L.a_s + T * kp // 32].view(T, kp // 32),
+            "A_s_raw": raw,
+            "A_s": raw.permute(1, 0, 2).reshape(T, kp // 32),
             "X_O": ws[L.x_o:L.x_o + T * kl * 2].view(torch.bfloat16).view(T, kl)}
 
 

@@ -85,16 +85,19 @@ typedef struct w4a4_packed {
     const int32_t* J;       /* device [k_j], ascending                                    */
     const uint8_t* B_q;     /* device [d_out][k_pad/2] E2M1 codes of fl32(s_j * W[n][j])  */
     const uint8_t* B_s;     /* device, E8M0 codes in the layout's shape (see enum)        */
-    const uint8_t* B_s_rows;/* device [d_out][k_pad/32]: the same codes expanded to one per
-                               row per 32-block (equals B_s for W4A4_WS_1X32; a derived
-                               copy for tiles and stripes that the GEMM streams)          */
+    const uint8_t* B_s_rows;/* device [k_pad/128][d_out][4]: the same codes, one per row per
+                               32-block, step-major (the four codes of a 128-code step of
+                               one row are adjacent, and consecutive rows follow), a
+                               derived copy that the GEMM streams                         */
     const uint16_t* W_O;    /* device bf16 [d_out][k_ld], raw W[n][O[i]], zero padded     */
 } w4a4_packed;
 
 /* Offsets (bytes) of the quantized activations inside a workspace. */
 typedef struct w4a4_ws_layout {
     size_t a_q;       /* uint8 [T][k_pad/2] activation E2M1 codes            */
-    size_t a_s;       /* uint8 [T][k_pad/32] activation E8M0 scales (1x32)    */
+    size_t a_s;       /* uint8 [k_pad/128][T][4] activation E8M0 scales (1x32),
+                         step-major: for each 128-code step the four codes of
+                         token t sit at [(step*T + t)*4 .. +3]                 */
     size_t x_o;       /* bf16  [T][k_ld] outlier columns, zero padded         */
     size_t total;     /* bytes needed                                         */
 } w4a4_ws_layout;
@@ -144,7 +147,8 @@ int w4a4_workspace_size(int64_t T, const w4a4_packed* desc, size_t* bytes);
 /* Act-prep (sec. 3.2 "divide by s, then quantize", sec. 3.3 split): X device
  * [T][d_in] fp32 or bf16, row-major contiguous.  For each token: x~ = fl32(x / s_j)
  * (IEEE binary32 division, subnormals kept) over the J columns in ascending order,
- * 1x32 E8M0 + E2M1 codes into A_q/A_s; X_O = bf16_rne(x) over the O columns.
+ * 1x32 E8M0 + E2M1 codes into A_q/A_s (A_s step-major, see w4a4_ws_layout);
+ * X_O = bf16_rne(x) over the O columns.
  * Async on `stream`; never allocates. */
 int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc,
                               void* ws, size_t ws_bytes, void* stream);

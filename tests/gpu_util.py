@@ -80,6 +80,17 @@ def _check_packed(r):
     if r["packed"].k_pad:
         assert np.array_equal(u8(v["B_q"]), pk["Bq"]), "B_q differs"
         assert np.array_equal(u8(v["B_s"]), pk["Bs"]), "B_s differs"
+        # the GEMM's step-major per-row copy holds the group code of every (row, 32-block)
+        d_out, K_pad, lay = pk["d_out"], pk["K_pad"], pk["layout"]
+        kb = np.arange(K_pad // 32)
+        nn = np.arange(d_out)
+        if lay == 0:
+            want = pk["Bs"]
+        elif lay == 2:
+            want = pk["Bs"][:, kb // 4]
+        else:
+            want = pk["Bs"][kb[None, :], (nn // 32)[:, None]]
+        assert np.array_equal(u8(v["B_s_rows"]), want), "B_s_rows differs"
     if k:
         wo = bf16_bits(v["W_O"])
         assert np.array_equal(wo[:, :k], pk["WO"]), "W_O differs"
