@@ -2,63 +2,74 @@
 // 2026 Challenge)", sec. 3.2: activations are divided by s and then quantized;
 // sec. 3.3: the static outlier columns O bypass quantization).
 //
-// One workgroup streams whole token rows (persistent over rows).  Per row:
-//   phase 1  each thread reads 8 consecutive input columns (one 16-byte load for
-//            bf16, two for fp32) and, through the column map, either writes
-//            x / s_j (IEEE binary32 division) into the LDS copy of the
-//            J-compacted row, or writes bf16(x) into X_O.  The column map and s
-//            for the thread's columns stay in registers across rows.
+// One workgroup streams whole token rows (persistent over rows) through an LDS copy
+// laid out as [k_pad] J-compacted smoothed values followed by [k_ld] outlier values.
+//   phase 1  every column goes to its fixed LDS slot, no branches: J column j at its
+//            compacted position as fl32(x / s_j) (IEEE binary32 division), outlier
+//            column O[i] at k_pad + i as the raw x.  Lane i of the workgroup owns the
+//            column pairs 2(i + 512m), 2(i+512m)+1 (one 4-byte load for bf16, 8 bytes
+//            for fp32, so each wavefront load is one contiguous run) and keeps their
+//            slots and s in registers for the whole launch.
 //   phase 2  each thread takes 8 consecutive compacted positions (two 16-byte LDS
-//            reads); four lanes form one 32-block, their |x| maxima meet through
-//            two xor-shuffles, and every lane emits 8 nibbles as one 32-bit store
-//            (lane 0 of the four also stores the E8M0 byte, into the step-major
-//            scale array [k_pad/128][T][4] that the GEMM streams contiguously).
-// HBM traffic is the algorithmic minimum: X read once, A_q/A_s/X_O written once.
+//            reads); four lanes form one 32-block and meet their |x| maxima through two
+//            DPP quad permutes; the E8M0 code follows from the maximum's exponent field
+//            and the eight E2M1 nibbles come from four scaled FP4 conversions
+//            (v_cvt_scalef32_pk_fp4_f32 with the scale 2^E as divisor), one 32-bit store
+//            per lane.  Lane 0 of the four stores the E8M0 byte into the step-major
+//            scale array [k_pad/128][T][4] that the GEMM streams contiguously.  X_O is
+//            copied out of the outlier slots as bf16.
+// Rows are loaded in batches of D rows per workgroup, the next batch issued while the
+// current one is processed, so that a full batch of loads is in flight across each
+// batch's work.  HBM traffic is the algorithmic minimum: X read once, A_q/A_s/X_O
+// written once.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
 
 namespace w4a4 {
 
+// Workgroup size of the generic kernel, and of the fast path up to d_in = 8192; the
+// fast path takes 1024 lanes up to d_in = 16384.
 constexpr int AP_THREADS = 512;
-constexpr int AP_COLS_PER_PASS = AP_THREADS * 8;
 
-template <typename XT>
-struct Vec8;
-template <>
-struct Vec8<uint16_t> {
-    __device__ static void load(const uint16_t* p, float* v) {
-        const uint4 q = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    }
-    __device__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
-};
-template <>
-struct Vec8<float> {
-    __device__ static void load(const float* p, float* v) {
-        const float4 a = reinterpret_cast<const float4*>(p)[0];
-        const float4 b = reinterpret_cast<const float4*>(p)[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-    __device__ static float load1(const float* p) { return *p; }
-};
-
-__device__ __forceinline__ void route(float x, int32_t m, float s, float* row, uint16_t* xo_row) {
-    if (m >= 0) row[m] = x / s;
-    else xo_row[-m - 1] = bf16_rne(x);
+// Rows per batch: within ~10 registers of row data per lane and per batch (one
+// register per bf16 pair, two per fp32 pair); two batches are live at once, and the
+// kernel stays within 128 VGPRs (four waves per SIMD: two 512-lane workgroups or one
+// 1024-lane workgroup per CU).
+template <typename XT, int MAXM>
+constexpr int ap_depth() {
+    constexpr int regs = MAXM * (int)(sizeof(XT) / 2);
+    return regs * 4 <= 10 ? 4 : regs * 3 <= 10 ? 3 : regs * 2 <= 10 ? 2 : 1;
 }
 
-// Phase 2 for one token row held in LDS.
+// Maximum of v over the four lanes of this lane's quad (lanes 4q..4q+3).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
+    return o > v ? o : v;
+}
+
+// Eight E2M1 nibbles (element 2i in the low nibble of byte i) for finite values whose
+// group scale code is `code` (< 0xFF).  The conversion divides by the fp32 scale 2^E
+// and rounds to nearest even, saturating at 6; E = -127 is the subnormal 2^-127.
+__device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
+    const float scale = __uint_as_float(code == 0u ? 0x00400000u : code << 23);
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+    return w;
+}
+
+// Phase 2 for one token row held in LDS (row[0, k_pad)).
 // as_t points at this token's scale slot of step 0 in the step-major A_s
-// ([k_pad/128][T][4]); step kb's slot is as_t + kb * as_step.
+// ([k_pad/128][T][4]); step kb's slot is as_t + kb * as_step.  k_pad is a multiple of
+// 128, so the four lanes of a quad are active together.
+template <int NT>
 __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, uint8_t* aq_row,
                                              uint8_t* as_t, int64_t as_step) {
-    for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += AP_COLS_PER_PASS) {
+    for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += NT * 8) {
         const float4 a = *reinterpret_cast<const float4*>(row + p0);
         const float4 b = *reinterpret_cast<const float4*>(row + p0 + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -68,98 +79,189 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
             const uint32_t q = abs_bits(v[i]);
             m = q > m ? q : m;
         }
-        uint32_t o = (uint32_t)__shfl_xor((int)m, 1);
-        m = o > m ? o : m;
-        o = (uint32_t)__shfl_xor((int)m, 2);
-        m = o > m ? o : m;
-        const uint32_t code = e8m0_from_absbits(m);
-        uint32_t word = 0;
-        if (code != 0xFFu) {
-            const float inv = e8m0_inverse(code);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) word |= e2m1_nibble(v[i], inv) << (4 * i);
-        }
+        const uint32_t code = e8m0_from_absbits(quad_max_u32(m));
+        const uint32_t word = code == 0xFFu ? 0u : e2m1_word8(v, code);
         *reinterpret_cast<uint32_t*>(aq_row + p0 / 2) = word;
         if ((threadIdx.x & 3) == 0) as_t[(p0 / 128) * as_step + (p0 / 32) % 4] = (uint8_t)code;
     }
 }
 
-// NCH > 0: d_in % 8 == 0, X 16-byte aligned, d_in <= NCH * AP_COLS_PER_PASS; the
-// column map and s of the thread's columns are cached in registers.
-template <typename XT, int NCH>
+// X_O row from the outlier slots row[k_pad, k_pad + k_ld) (slots >= k hold zero).
+template <int NT>
+__device__ __forceinline__ void copy_outliers(const float* row, int64_t k_pad, int64_t k_ld, uint16_t* xo_row) {
+    for (int64_t i = threadIdx.x; i < k_ld; i += NT) xo_row[i] = bf16_rne(row[k_pad + i]);
+}
+
+// Fixed LDS slot of input column j from its column-map entry.
+__device__ __forceinline__ int32_t slot_of(int32_t m, int64_t k_pad) {
+    return m >= 0 ? m : (int32_t)k_pad + (-m - 1);
+}
+
+// Zero the parts of the LDS row that phase 1 never writes: the J tail [k_j, k_pad)
+// and the unused outlier slots [k_pad + k, k_pad + k_ld).
+template <int NT>
+__device__ __forceinline__ void zero_pads(float* row, int64_t k_j, int64_t k_pad, int32_t k, int64_t k_ld) {
+    for (int64_t p = k_j + threadIdx.x; p < k_pad; p += NT) row[p] = 0.0f;
+    for (int64_t p = k_pad + k + threadIdx.x; p < k_pad + k_ld; p += NT) row[p] = 0.0f;
+}
+
+template <typename XT>
+__device__ __forceinline__ float load1(const XT* p);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+
+// Generic path: any d_in, any element alignment of X.  One column per lane per pass.
+template <typename XT>
 __global__ __launch_bounds__(AP_THREADS) void actprep_kernel(
     const XT* __restrict__ X, int64_t T, int64_t d_in, const int32_t* __restrict__ colmap,
     const float* __restrict__ s, int64_t k_j, int64_t k_pad, int32_t k, int64_t k_ld,
     uint8_t* __restrict__ Aq, uint8_t* __restrict__ As, uint16_t* __restrict__ XO) {
     extern __shared__ float row[];
-    for (int64_t p = k_j + threadIdx.x; p < k_pad; p += AP_THREADS) row[p] = 0.0f;
-
-    int32_t cm[NCH > 0 ? NCH : 1][8];
-    float sv[NCH > 0 ? NCH : 1][8];
-    if constexpr (NCH > 0) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int64_t j0 = (int64_t)c * AP_COLS_PER_PASS + threadIdx.x * 8;
-            if (j0 < d_in) {
-                const int4 m0 = reinterpret_cast<const int4*>(colmap + j0)[0];
-                const int4 m1 = reinterpret_cast<const int4*>(colmap + j0)[1];
-                const float4 s0 = reinterpret_cast<const float4*>(s + j0)[0];
-                const float4 s1 = reinterpret_cast<const float4*>(s + j0)[1];
-                cm[c][0] = m0.x; cm[c][1] = m0.y; cm[c][2] = m0.z; cm[c][3] = m0.w;
-                cm[c][4] = m1.x; cm[c][5] = m1.y; cm[c][6] = m1.z; cm[c][7] = m1.w;
-                sv[c][0] = s0.x; sv[c][1] = s0.y; sv[c][2] = s0.z; sv[c][3] = s0.w;
-                sv[c][4] = s1.x; sv[c][5] = s1.y; sv[c][6] = s1.z; sv[c][7] = s1.w;
-            }
-        }
-    }
-
+    zero_pads<AP_THREADS>(row, k_j, k_pad, k, k_ld);
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         const XT* xr = X + t * d_in;
-        uint16_t* xo_row = XO + t * k_ld;
-        if constexpr (NCH > 0) {
+        for (int64_t j = threadIdx.x; j < d_in; j += AP_THREADS) {
+            const int32_t m = colmap[j];
+            const float x = load1<XT>(xr + j);
+            row[slot_of(m, k_pad)] = m >= 0 ? x / s[j] : x;
+        }
+        __syncthreads();
+        quantize_row<AP_THREADS>(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
+        copy_outliers<AP_THREADS>(row, k_pad, k_ld, XO + t * k_ld);
+        __syncthreads();
+    }
+}
+
+template <typename XT>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+    typedef uint32_t raw;
+    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    __device__ static float lo(raw r) { return __uint_as_float(r << 16); }
+    __device__ static float hi(raw r) { return __uint_as_float(r & 0xFFFF0000u); }
+};
+template <>
+struct Pair<float> {
+    typedef float2 raw;
+    __device__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    __device__ static float lo(raw r) { return r.x; }
+    __device__ static float hi(raw r) { return r.y; }
+};
+
+// Fast path: d_in even, X 8-byte aligned, d_in <= 2 * NT * MAXM.
+template <typename XT, int NT, int MAXM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void actprep_pairs_kernel(
+    const XT* __restrict__ X, int64_t T, int64_t d_in, const int32_t* __restrict__ colmap,
+    const float* __restrict__ s, int64_t k_j, int64_t k_pad, int32_t k, int64_t k_ld,
+    uint8_t* __restrict__ Aq, uint8_t* __restrict__ As, uint16_t* __restrict__ XO) {
+    extern __shared__ float row[];
+    zero_pads<NT>(row, k_j, k_pad, k, k_ld);
+
+    // Loads are never predicated (lanes past the last pair re-read it, rows past T
+    // re-read row T-1) so that the compiler sees every load of a batch complete at the
+    // batch's first wait; only the LDS writes of lanes past the last pair are skipped.
+    const int64_t npairs = d_in / 2;
+    int32_t slot[MAXM][2];
+    float sv[MAXM][2];
+    bool outl[MAXM][2];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int64_t j0 = (int64_t)c * AP_COLS_PER_PASS + threadIdx.x * 8;
-                if (j0 < d_in) {
-                    float v[8];
-                    Vec8<XT>::load(xr + j0, v);
+    for (int m = 0; m < MAXM; ++m) {
+        const int64_t pi = min((int64_t)threadIdx.x + (int64_t)NT * m, npairs - 1);
+        const int2 cm = reinterpret_cast<const int2*>(colmap)[pi];
+        const float2 s2 = reinterpret_cast<const float2*>(s)[pi];
+        slot[m][0] = slot_of(cm.x, k_pad);
+        slot[m][1] = slot_of(cm.y, k_pad);
+        sv[m][0] = s2.x;
+        sv[m][1] = s2.y;
+        outl[m][0] = cm.x < 0;
+        outl[m][1] = cm.y < 0;
+    }
+
+    constexpr int D = ap_depth<XT, MAXM>();
+    typedef typename Pair<XT>::raw raw;
+    const int64_t G = gridDim.x;
+    auto row_of = [&](int64_t r) __attribute__((always_inline)) { return (int64_t)blockIdx.x + r * G; };
+    auto fetch = [&](raw (*xv)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) route(v[e], cm[c][e], sv[c][e], row, xo_row);
+        for (int d = 0; d < D; ++d) {
+            const XT* xr = X + min(row_of(r0 + d), T - 1) * d_in;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const int64_t pi = min((int64_t)threadIdx.x + (int64_t)NT * m, npairs - 1);
+                xv[d][m] = Pair<XT>::load(xr + 2 * pi);
+            }
+        }
+    };
+    // Rows r0 .. r0+D-1 of this workgroup from xv; the loads of the next batch into
+    // xn are issued once the first row of this batch has left the registers.
+    auto batch = [&](raw (*xv)[MAXM], raw (*xn)[MAXM], int64_t r0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t t = row_of(r0 + d);
+            if (t >= T) break;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const float lo = Pair<XT>::lo(xv[d][m]), hi = Pair<XT>::hi(xv[d][m]);
+                const float qlo = lo / sv[m][0], qhi = hi / sv[m][1];
+                if ((int64_t)threadIdx.x + (int64_t)NT * m < npairs) {
+                    row[slot[m][0]] = outl[m][0] ? lo : qlo;
+                    row[slot[m][1]] = outl[m][1] ? hi : qhi;
                 }
             }
-        } else {
-            for (int64_t j = threadIdx.x; j < d_in; j += AP_THREADS)
-                route(Vec8<XT>::load1(xr + j), colmap[j], s[j], row, xo_row);
+            if (d == 0) fetch(xn, r0 + D);
+            __syncthreads();
+            quantize_row<NT>(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
+            copy_outliers<NT>(row, k_pad, k_ld, XO + t * k_ld);
+            __syncthreads();
         }
-        for (int64_t i = k + threadIdx.x; i < k_ld; i += AP_THREADS) xo_row[i] = 0;
-        __syncthreads();
-        quantize_row(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
-        __syncthreads();
+    };
+    raw xa[D][MAXM], xb[D][MAXM];
+    fetch(xa, 0);
+    for (int64_t r = 0; row_of(r) < T; r += 2 * D) {
+        batch(xa, xb, r);
+        if (row_of(r + D) >= T) break;
+        batch(xb, xa, r + D);
     }
 }
 
 template <typename XT>
 static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uint8_t* Aq, uint8_t* As,
                                uint16_t* XO, hipStream_t st) {
-    const size_t lds = (size_t)(d.k_pad > 0 ? d.k_pad : 1) * sizeof(float);
+    const size_t lds = (size_t)(d.k_pad + d.k_ld > 0 ? d.k_pad + d.k_ld : 1) * sizeof(float);
     const int64_t grid64 = T < 2048 ? T : 2048;
     const unsigned grid = (unsigned)grid64;
-    const bool vec = (d.d_in % 8 == 0) && (((uintptr_t)X & 15u) == 0);
-    const int nch = (int)((d.d_in + AP_COLS_PER_PASS - 1) / AP_COLS_PER_PASS);
-#define W4A4_AP_CALL(N)                                                                              \
-    if (lds > 65536) {                                                                               \
-        hipError_t e = hipFuncSetAttribute((const void*)actprep_kernel<XT, N>,                       \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
-        if (e != hipSuccess) return e;                                                               \
-    }                                                                                                \
-    actprep_kernel<XT, N><<<grid, AP_THREADS, lds, st>>>(X, T, d.d_in, d.colmap, d.s, d.k_j, d.k_pad, \
-                                                         d.k, d.k_ld, Aq, As, XO)
-    if (vec && nch <= 1) { W4A4_AP_CALL(1); }
-    else if (vec && nch == 2) { W4A4_AP_CALL(2); }
-    else if (vec && nch <= 4) { W4A4_AP_CALL(4); }
-    else { W4A4_AP_CALL(0); }
-#undef W4A4_AP_CALL
-    return hipGetLastError();
+    const bool pairs = (d.d_in % 2 == 0) && (((uintptr_t)X & 7u) == 0);
+    const int64_t npairs = d.d_in / 2;
+#define W4A4_AP_LAUNCH(KERNEL, NT)                                                                   \
+    {                                                                                                \
+        if (lds > 65536) {                                                                           \
+            hipError_t e = hipFuncSetAttribute((const void*)KERNEL,                                  \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+            if (e != hipSuccess) return e;                                                           \
+        }                                                                                            \
+        KERNEL<<<grid, NT, lds, st>>>(X, T, d.d_in, d.colmap, d.s, d.k_j, d.k_pad, d.k, d.k_ld, Aq, \
+                                      As, XO);                                                       \
+        return hipGetLastError();                                                                    \
+    }
+#define W4A4_AP_PAIRS(NT, M) \
+    if (pairs && npairs <= (int64_t)(NT) * (M)) W4A4_AP_LAUNCH((actprep_pairs_kernel<XT, NT, M>), NT)
+    W4A4_AP_PAIRS(512, 1)
+    W4A4_AP_PAIRS(512, 2)
+    W4A4_AP_PAIRS(512, 3)
+    W4A4_AP_PAIRS(512, 4)
+    W4A4_AP_PAIRS(512, 5)
+    W4A4_AP_PAIRS(512, 6)
+    W4A4_AP_PAIRS(512, 8)
+    W4A4_AP_PAIRS(1024, 5)
+    W4A4_AP_PAIRS(1024, 6)
+    W4A4_AP_PAIRS(1024, 7)
+    W4A4_AP_PAIRS(1024, 8)
+    W4A4_AP_LAUNCH((actprep_kernel<XT>), AP_THREADS)
+#undef W4A4_AP_PAIRS
+#undef W4A4_AP_LAUNCH
 }
 
 hipError_t launch_actprep(const void* X, int x_dtype, int64_t T, const w4a4_packed& d, uint8_t* Aq,
