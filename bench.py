@@ -89,6 +89,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run 4 plain device-to-device copies of this "
+                         "many MiB (the known-size kernel that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -97,6 +100,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 4 copies of {n} bytes (read {n} + write {n} per copy)")
+        return
 
     from bit_quantized_dit_amd import synth
     from bit_quantized_dit_amd import w4a4 as B

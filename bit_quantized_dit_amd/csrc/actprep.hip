@@ -182,12 +182,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
 
     constexpr int D = ap_depth<XT, MAXM>();
     typedef typename Pair<XT>::raw raw;
-    const int64_t G = gridDim.x;
-    auto row_of = [&](int64_t r) __attribute__((always_inline)) { return (int64_t)blockIdx.x + r * G; };
+    // Each workgroup owns a contiguous range of tokens, so the 4-byte A_s slots of
+    // neighbouring tokens (one 64-byte line per 16 tokens and step) are written from
+    // one CU and one L2 rather than as partial lines from several XCDs.
+    const int64_t per_wg = (T + gridDim.x - 1) / gridDim.x;
+    const int64_t t_begin = (int64_t)blockIdx.x * per_wg;
+    const int64_t t_end = min(T, t_begin + per_wg);
+    if (t_begin >= t_end) return;
+    auto row_of = [&](int64_t r) __attribute__((always_inline)) { return t_begin + r; };
     auto fetch = [&](raw (*xv)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const XT* xr = X + min(row_of(r0 + d), T - 1) * d_in;
+            const XT* xr = X + min(row_of(r0 + d), t_end - 1) * d_in;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 const int64_t pi = min((int64_t)threadIdx.x + (int64_t)NT * m, npairs - 1);
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int64_t t = row_of(r0 + d);
-            if (t >= T) break;
+            if (t >= t_end) break;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 const float lo = Pair<XT>::lo(xv[d][m]), hi = Pair<XT>::hi(xv[d][m]);
@@ -220,9 +226,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     };
     raw xa[D][MAXM], xb[D][MAXM];
     fetch(xa, 0);
-    for (int64_t r = 0; row_of(r) < T; r += 2 * D) {
+    for (int64_t r = 0; row_of(r) < t_end; r += 2 * D) {
         batch(xa, xb, r);
-        if (row_of(r + D) >= T) break;
+        if (row_of(r + D) >= t_end) break;
         batch(xb, xa, r + D);
     }
 }
