@@ -15,7 +15,7 @@
 //            DPP quad permutes; the E8M0 code follows from the maximum's exponent field
 //            and the eight E2M1 nibbles come from four scaled FP4 conversions
 //            (v_cvt_scalef32_pk_fp4_f32 with the scale 2^E as divisor), one 32-bit store
-//            per lane.  Lane 0 of the four stores the E8M0 byte into the step-major
+//            per lane into A_q in the GEMM's tiled order.  Lane 0 of the four stores the E8M0 byte into the step-major
 //            scale array [k_pad/128][T][4] that the GEMM streams contiguously.  X_O is
 //            copied out of the outlier slots as bf16.
 // Rows are loaded in batches of D rows per workgroup, the next batch issued while the
@@ -62,13 +62,17 @@ __device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
     return w;
 }
 
-// Phase 2 for one token row held in LDS (row[0, k_pad)).
+// Phase 2 for token t held in LDS (row[0, k_pad)).
+// A_q is written in the GEMM's tiled order: 1 KiB per (16-token block, 128-code step),
+// token t % 16 at 64-byte stride, 16-byte chunk c at chunk position c ^ ((t % 16) / 4).
 // as_t points at this token's scale slot of step 0 in the step-major A_s
 // ([k_pad/128][T][4]); step kb's slot is as_t + kb * as_step.  k_pad is a multiple of
 // 128, so the four lanes of a quad are active together.
 template <int NT>
-__device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, uint8_t* aq_row,
+__device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, uint8_t* Aq, int64_t t,
                                              uint8_t* as_t, int64_t as_step) {
+    const int r = (int)(t & 15);
+    uint8_t* aq_blk = Aq + (((t >> 4) * (k_pad / 128)) << 10) + (r << 6);
     for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += NT * 8) {
         const float4 a = *reinterpret_cast<const float4*>(row + p0);
         const float4 b = *reinterpret_cast<const float4*>(row + p0 + 4);
@@ -81,7 +85,8 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
         }
         const uint32_t code = e8m0_from_absbits(quad_max_u32(m));
         const uint32_t word = code == 0xFFu ? 0u : e2m1_word8(v, code);
-        *reinterpret_cast<uint32_t*>(aq_row + p0 / 2) = word;
+        const int byte = (int)(p0 % 128) / 2;   // within the 64-byte row slice of the step
+        *reinterpret_cast<uint32_t*>(aq_blk + ((p0 / 128) << 10) + ((((byte >> 4) ^ (r >> 2)) << 4) | (byte & 15))) = word;
         if ((threadIdx.x & 3) == 0) as_t[(p0 / 128) * as_step + (p0 / 32) % 4] = (uint8_t)code;
     }
 }
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(AP_THREADS) void actprep_kernel(
             row[slot_of(m, k_pad)] = m >= 0 ? x / s[j] : x;
         }
         __syncthreads();
-        quantize_row<AP_THREADS>(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
+        quantize_row<AP_THREADS>(row, k_pad, Aq, t, As + t * 4, T * 4);
         copy_outliers<AP_THREADS>(row, k_pad, k_ld, XO + t * k_ld);
         __syncthreads();
     }
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
             }
             if (d == 0) fetch(xn, r0 + D);
             __syncthreads();
-            quantize_row<NT>(row, k_pad, Aq + t * (k_pad / 2), As + t * 4, T * 4);
+            quantize_row<NT>(row, k_pad, Aq, t, As + t * 4, T * 4);
             copy_outliers<NT>(row, k_pad, k_ld, XO + t * k_ld);
             __syncthreads();
         }

@@ -31,7 +31,7 @@ int64_t weight_scale_bytes(int64_t d_out, int64_t k_pad, int layout) {
 }
 
 struct BlobLayout {
-    size_t colmap, s, O, J, B_q, B_s, B_s_rows, W_O, total;
+    size_t colmap, s, O, J, B_q, B_s, B_s_rows, W_O, B_q_tiles, total;
 };
 
 BlobLayout blob_layout(int64_t d_in, int64_t d_out, int32_t k, int layout) {
@@ -48,6 +48,7 @@ BlobLayout blob_layout(int64_t d_in, int64_t d_out, int32_t k, int layout) {
     b.B_s = off;    off = align_up(off + (size_t)weight_scale_bytes(d_out, k_pad, layout));
     b.B_s_rows = off;     off = align_up(off + (size_t)(d_out * (k_pad / 32)));
     b.W_O = off;    off = align_up(off + (size_t)(d_out * k_ld) * 2);
+    b.B_q_tiles = off; off = align_up(off + (size_t)(round_up(d_out, 16) * (k_pad / 2)));
     b.total = off;
     return b;
 }
@@ -71,9 +72,11 @@ int check_desc(const w4a4_packed* d) {
     if (d->k_j != d->d_in - d->k || d->k_pad != round_up(d->k_j, 128) || d->k_ld != round_up(d->k, 32))
         return W4A4_ERR_INVALID;
     if (!d->colmap || !d->s) return W4A4_ERR_INVALID;
-    if (d->k_pad > 0 && (!d->B_q || !d->B_s || !d->B_s_rows || !d->J)) return W4A4_ERR_INVALID;
+    if (d->k_pad > 0 && (!d->B_q || !d->B_s || !d->B_s_rows || !d->B_q_tiles || !d->J))
+        return W4A4_ERR_INVALID;
     if (d->k > 0 && (!d->W_O || !d->O)) return W4A4_ERR_INVALID;
-    if (misaligned(d->colmap) || misaligned(d->s) || misaligned(d->B_q) || misaligned(d->W_O))
+    if (misaligned(d->colmap) || misaligned(d->s) || misaligned(d->B_q) || misaligned(d->W_O) ||
+        misaligned(d->B_q_tiles))
         return W4A4_ERR_ALIGN;
     return W4A4_OK;
 }
@@ -81,7 +84,7 @@ int check_desc(const w4a4_packed* d) {
 w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) {
     w4a4_ws_layout w;
     size_t off = 0;
-    w.a_q = off; off = align_up(off + (size_t)(T * (d->k_pad / 2)));
+    w.a_q = off; off = align_up(off + (size_t)(round_up(T, 16) * (d->k_pad / 2)));
     w.a_s = off; off = align_up(off + (size_t)(T * (d->k_pad / 32)));
     w.x_o = off; off = align_up(off + (size_t)(T * d->k_ld) * 2);
     w.total = off;
@@ -206,6 +209,7 @@ int w4a4_pack_weights(const float* W, int64_t d_in, int64_t d_out, const float* 
     d.B_q = base + b.B_q;
     d.B_s = base + b.B_s;
     d.B_s_rows = base + b.B_s_rows;
+    d.B_q_tiles = base + b.B_q_tiles;
     d.W_O = (const uint16_t*)(base + b.W_O);
 
     hipStream_t hs = (hipStream_t)stream;

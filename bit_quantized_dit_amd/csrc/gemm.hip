@@ -18,6 +18,10 @@
 // chunk; lane l of the result holds token l%32 and features 8q + 4(l/32) + r, r < 4,
 // in registers 4q + r, stored as four float4.
 //
+// Operand layout: both code operands arrive in the tiled order (1 KiB per 16-row
+// block and 128-code step, chunk-swizzled as in LDS), so every DMA instruction reads
+// one contiguous KiB; the step-major scale words are one contiguous run per step.
+//
 // Tiling: a 512-thread workgroup (8 wavefronts, 2 token halves x 4 feature quarters,
 // two per SIMD) owns a 256-token x 256-feature output tile; each wavefront a
 // 128 x 64 sub-tile (4 x 2 MFMA tiles, 128 fp32 accumulators per lane in AGPRs), so
@@ -32,9 +36,9 @@
 // the outlier branch: 32 bf16 values of X_O and W_O per row are again 64 bytes, so
 // each BF16 step has the slot layout of an FP4 step (without scales) and feeds
 // v_mfma_f32_32x32x16_bf16 into the same accumulators.
-// 16-byte chunks are XOR-swizzled by row
-// (the swizzle is applied to the global source address, since the DMA writes each
-// wavefront's 1 KiB contiguously) so that fragment reads are bank-conflict free.
+// 16-byte chunks are XOR-swizzled by row so that fragment reads are bank-conflict
+// free (the DMA writes each wavefront's 1 KiB contiguously, so the swizzle lives in
+// the tiled code layout, and in the source addresses of the bf16 gather).
 // Buffer descriptors cover exactly the tile's valid rows: rows past the token or
 // feature tail read as zero, with no masking in the loop.
 //
@@ -153,7 +157,6 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int64_t a_ld = k_pad / 2;      // bytes per row of A_q / B_q
     const int64_t o_ld = k_ld * 2;       // bytes per row of X_O / W_O
     const int nkb = (int)(k_pad / 128);  // FP4 steps (128 codes = 64 bytes per row)
     const int nbf = (int)(k_ld / 32);    // BF16 steps (32 values = 64 bytes per row)
@@ -162,8 +165,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     if (nsteps > 0) {
         const int64_t rows_a = T - t0 < BT ? T - t0 : BT;
         const int64_t rows_b = N - f0 < BF ? N - f0 : BF;
-        const v4i srdA = make_srd(Aq + t0 * a_ld, (uint32_t)(rows_a * a_ld));
-        const v4i srdB = make_srd(Bq + f0 * a_ld, (uint32_t)(rows_b * a_ld));
+        // FP4 codes in the tiled order (1 KiB per 16-row block and step, the LDS
+        // swizzle already applied): a tile's 16 row blocks start blk bytes apart.
+        const int64_t blk = (int64_t)nkb * 1024;
+        const v4i srdA = make_srd(Aq + (t0 / 16) * blk, (uint32_t)((rows_a + 15) / 16 * blk));
+        const v4i srdB = make_srd(Bq + (f0 / 16) * blk, (uint32_t)((rows_b + 15) / 16 * blk));
         // Step-major scales: step st's words of this tile's rows start at
         // (st * rows_total + row0) * 4.  The step offset goes into the descriptor base
         // (not soffset, which the range check does not cover), so the descriptor spans
@@ -176,15 +182,17 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         const v4i srdWO = make_srd(WO + f0 * k_ld, (uint32_t)(rows_b * o_ld));
         const v4i srd0 = make_srd(Aq, 0u);
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-        // per-lane source offsets of this wavefront's four 1 KiB row blocks: block b
-        // covers rows 16b..16b+15; lane -> row 16b + lane/4, physical chunk lane%4,
-        // logical chunk = physical ^ ((row >> 2) & 3); one set per row stride
+        // per-lane source offsets of this wavefront's two 1 KiB row blocks per operand:
+        // block b covers rows 16b..16b+15 and lands at LDS b*1024 as it lies in memory
+        // for the FP4 codes (lane -> 16 contiguous bytes); the row-major bf16 outlier
+        // operands are gathered into the same order: lane -> row 16b + lane/4, physical
+        // chunk lane%4, logical chunk = physical ^ ((row >> 2) & 3)
         int voff[2], voffo[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = 16 * (wave * 2 + h) + (lane >> 2);
             const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
-            voff[h] = row * (int)a_ld + chunk;
+            voff[h] = (wave * 2 + h) * (int)blk + lane * 16;
             voffo[h] = row * (int)o_ld + chunk;
         }
         // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             r.b = pick(fp4, srdB, bf, srdWO);
             r.as = pick(fp4, scale_srd(As, fp4 ? st : 0, T, t0, rows_a), false, srd0);
             r.bs = pick(fp4, scale_srd(Bs_rows, fp4 ? st : 0, N, f0, rows_b), false, srd0);
-            r.so = fp4 ? st * 64 : (bf ? (st - nkb) * 64 : 0);
+            r.so = fp4 ? st * 1024 : (bf ? (st - nkb) * 64 : 0);
             r.ss = 0;
             return r;
         };
@@ -415,7 +423,7 @@ hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
     if ((int64_t)BT * (d.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)Y & 15u) == 0);
     gemm_w4a4_kernel<<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
-        Aq, As, XO, T, d.B_q, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, Y, vec_store);
+        Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, Y, vec_store);
     return hipGetLastError();
 }
 

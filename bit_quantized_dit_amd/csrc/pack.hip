@@ -52,31 +52,44 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const float* __restric
     Bs[g] = (uint8_t)e8m0_from_absbits(m);
 }
 
-// Pass 2: one thread per (row n, 32-block kb): 32 codes -> 16 bytes.
+// Byte offset of the 16-byte chunk c (0..3) of row n, 128-code step kb, in the tiled
+// copy: 1 KiB per (16-row block, step), row n % 16 at 64-byte stride, chunk c at
+// chunk position c ^ ((n % 16) / 4) (the order the GEMM's LDS ring uses).
+__device__ __forceinline__ int64_t tiled_chunk(int64_t n, int64_t kb, int64_t nkb, int c) {
+    const int r = (int)(n & 15);
+    return (((n >> 4) * nkb + kb) << 10) + (r << 6) + ((c ^ (r >> 2)) << 4);
+}
+
+// Pass 2: one thread per (row n, 32-block kb): 32 codes -> 16 bytes, written to the
+// canonical B_q and to the tiled copy (rows d_out .. roundup(d_out, 16) are zero there).
 __global__ __launch_bounds__(256) void pack_codes_kernel(const float* __restrict__ W,
                                                          const float* __restrict__ s,
                                                          const int32_t* __restrict__ J, int64_t d_in,
                                                          int64_t d_out, int64_t k_j, int64_t k_pad,
                                                          int layout, const uint8_t* __restrict__ Bs,
-                                                         uint8_t* __restrict__ Bq) {
+                                                         uint8_t* __restrict__ Bq, uint8_t* __restrict__ Bqt) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nkb = k_pad / 32;
-    if (g >= d_out * nkb) return;
+    const int64_t rows = (d_out + 15) / 16 * 16;
+    if (g >= rows * nkb) return;
     const int64_t n = g / nkb, kb = g % nkb;
-    uint32_t code;
-    if (layout == W4A4_WS_1X32) code = Bs[n * nkb + kb];
-    else if (layout == W4A4_WS_128X1_STRIPE) code = Bs[n * (k_pad / 128) + kb / 4];
-    else code = Bs[kb * ((d_out + 31) / 32) + n / 32];
     uint32_t words[4] = {0u, 0u, 0u, 0u};
-    if (code != 0xFFu) {
-        const float inv = e8m0_inverse(code);
-        for (int i = 0; i < 32; ++i) {
-            const float w = folded(W, s, J, d_in, k_j, n, kb * 32 + i);
-            words[i >> 3] |= e2m1_nibble(w, inv) << (4 * (i & 7));
+    if (n < d_out) {
+        uint32_t code;
+        if (layout == W4A4_WS_1X32) code = Bs[n * nkb + kb];
+        else if (layout == W4A4_WS_128X1_STRIPE) code = Bs[n * (k_pad / 128) + kb / 4];
+        else code = Bs[kb * ((d_out + 31) / 32) + n / 32];
+        if (code != 0xFFu) {
+            const float inv = e8m0_inverse(code);
+            for (int i = 0; i < 32; ++i) {
+                const float w = folded(W, s, J, d_in, k_j, n, kb * 32 + i);
+                words[i >> 3] |= e2m1_nibble(w, inv) << (4 * (i & 7));
+            }
         }
+        *reinterpret_cast<uint4*>(Bq + n * (k_pad / 2) + kb * 16) = make_uint4(words[0], words[1], words[2], words[3]);
     }
-    uint4* dst = reinterpret_cast<uint4*>(Bq + n * (k_pad / 2) + kb * 16);
-    *dst = make_uint4(words[0], words[1], words[2], words[3]);
+    *reinterpret_cast<uint4*>(Bqt + tiled_chunk(n, kb / 4, k_pad / 128, (int)(kb % 4))) =
+        make_uint4(words[0], words[1], words[2], words[3]);
 }
 
 // Step-major per-row copy of the weight scales: for each 128-code step kb, row n's
@@ -120,8 +133,9 @@ hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st) {
                                                                d.k_pad, d.layout, (uint8_t*)d.B_s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        pack_codes_kernel<<<blocks_for(d.d_out * (d.k_pad / 32)), 256, 0, st>>>(
-            W, d.s, d.J, d.d_in, d.d_out, d.k_j, d.k_pad, d.layout, d.B_s, (uint8_t*)d.B_q);
+        pack_codes_kernel<<<blocks_for((d.d_out + 15) / 16 * 16 * (d.k_pad / 32)), 256, 0, st>>>(
+            W, d.s, d.J, d.d_in, d.d_out, d.k_j, d.k_pad, d.layout, d.B_s, (uint8_t*)d.B_q,
+            (uint8_t*)d.B_q_tiles);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         pack_row_scales_kernel<<<blocks_for(d.d_out * (d.k_pad / 32)), 256, 0, st>>>(

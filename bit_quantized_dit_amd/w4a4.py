@@ -36,7 +36,8 @@ class W4A4Packed(ctypes.Structure):
                 ("layout", ctypes.c_int32), ("k_j", ctypes.c_int64), ("k_pad", ctypes.c_int64),
                 ("k_ld", ctypes.c_int64), ("colmap", ctypes.c_void_p), ("s", ctypes.c_void_p),
                 ("O", ctypes.c_void_p), ("J", ctypes.c_void_p), ("B_q", ctypes.c_void_p),
-                ("B_s", ctypes.c_void_p), ("B_s_rows", ctypes.c_void_p), ("W_O", ctypes.c_void_p)]
+                ("B_s", ctypes.c_void_p), ("B_s_rows", ctypes.c_void_p), ("W_O", ctypes.c_void_p),
+                ("B_q_tiles", ctypes.c_void_p)]
 
 
 class W4A4WsLayout(ctypes.Structure):
@@ -165,6 +166,10 @@ class PackedLayer:
             raw = view(d.B_s_rows, d.d_out * d.k_pad // 32, torch.uint8, (d.k_pad // 128, d.d_out, 4))
             out["B_s_rows_raw"] = raw
             out["B_s_rows"] = raw.permute(1, 0, 2).reshape(d.d_out, d.k_pad // 32)
+            rows16 = (d.d_out + 15) // 16 * 16
+            tiles = view(d.B_q_tiles, rows16 * d.k_pad // 2, torch.uint8, (rows16 * d.k_pad // 2,))
+            out["B_q_tiles_raw"] = tiles
+            out["B_q_from_tiles"] = untile_codes(tiles, rows16, d.k_pad)[:d.d_out]
         if d.k:
             out["W_O"] = view(d.W_O, d.d_out * d.k_ld * 2, torch.bfloat16, (d.d_out, d.k_ld))
             out["O"] = view(d.O, d.k * 4, torch.int32, (d.k,))
@@ -243,18 +248,34 @@ def w4a4_workspace_size(T: int, packed: PackedLayer) -> int:
     return n.value
 
 
+def untile_codes(raw: torch.Tensor, rows: int, k_pad: int) -> torch.Tensor:
+    """[rows, k_pad/2] row-major copy of codes stored in the tiled order (1 KiB per
+    16-row block and 128-code step; row r of a block at r*64, its 16-byte chunk c at
+    chunk position c ^ (r // 4)).  rows is a multiple of 16."""
+    nkb = k_pad // 128
+    t = raw.view(rows // 16, nkb, 16, 4, 16)
+    r = torch.arange(16, device=raw.device).view(16, 1)
+    phys = torch.arange(4, device=raw.device).view(1, 4) ^ (r // 4)     # [16, 4]: chunk c -> position
+    t = t[:, :, r, phys, :]                                              # [blocks, nkb, 16, 4, 16]
+    return t.permute(0, 2, 1, 3, 4).reshape(rows, k_pad // 2)
+
+
 def alloc_workspace(T: int, packed: PackedLayer, device="cuda") -> torch.Tensor:
     return torch.empty(max(w4a4_workspace_size(T, packed), 256), dtype=torch.uint8, device=device)
 
 
 def workspace_views(ws: torch.Tensor, T: int, packed: PackedLayer) -> dict:
-    """Device tensors of the quantized activations inside ws: A_q [T, k_pad/2],
-    X_O [T, k_ld], A_s_raw (the step-major [k_pad/128, T, 4] array) and A_s (the same
-    codes as a [T, k_pad/32] copy)."""
+    """Device tensors of the quantized activations inside ws: A_q_raw (the tiled
+    array), A_q (the same codes as a [T, k_pad/2] copy), X_O [T, k_ld], A_s_raw (the
+    step-major [k_pad/128, T, 4] array) and A_s (the same codes as a [T, k_pad/32]
+    copy)."""
     L = w4a4_workspace_layout(T, packed)
     kp, kl = packed.k_pad, packed.k_ld
     raw = ws[L.a_s:L.a_s + T * kp // 32].view(kp // 128, T, 4)
-    return {"A_q": ws[L.a_q:L.a_q + T * kp // 2].view(T, kp // 2),
+    rows16 = (T + 15) // 16 * 16
+    aq_raw = ws[L.a_q:L.a_q + rows16 * kp // 2]
+    return {"A_q_raw": aq_raw,
+            "A_q": untile_codes(aq_raw, rows16, kp)[:T],
             "A_s_raw": raw,
             "A_s": raw.permute(1, 0, 2).reshape(T, kp // 32),
             "X_O": ws[L.x_o:L.x_o + T * kl * 2].view(torch.bfloat16).view(T, kl)}

@@ -90,11 +90,22 @@ typedef struct w4a4_packed {
                                one row are adjacent, and consecutive rows follow), a
                                derived copy that the GEMM streams                         */
     const uint16_t* W_O;    /* device bf16 [d_out][k_ld], raw W[n][O[i]], zero padded     */
+    const uint8_t* B_q_tiles;/* device, the codes of B_q re-laid for the GEMM's DMA (a derived
+                               copy): [ceil(d_out/16)][k_pad/128][16][64] -- for each block of
+                               16 rows and each 128-code step one contiguous 1 KiB run, row r
+                               of the block at r*64, its 16-byte chunk c at chunk position
+                               c ^ ((r >> 2) & 3); rows past d_out are zero                 */
 } w4a4_packed;
 
 /* Offsets (bytes) of the quantized activations inside a workspace. */
 typedef struct w4a4_ws_layout {
-    size_t a_q;       /* uint8 [T][k_pad/2] activation E2M1 codes            */
+    size_t a_q;       /* uint8 activation E2M1 codes in the GEMM's tiled order,
+                         [ceil(T/16)][k_pad/128][16][64]: the byte holding codes
+                         p, p+1 (p even) of token t sits at
+                           ((t/16)*(k_pad/128) + p/128)*1024 + (t%16)*64
+                           + (c ^ ((t%16)/4))*16 + ((p%128)/2)%16,
+                         c = (p%128)/32 -- the order of B_q_tiles; rows past T
+                         inside the last 16-row block are left unwritten     */
     size_t a_s;       /* uint8 [k_pad/128][T][4] activation E8M0 scales (1x32),
                          step-major: for each 128-code step the four codes of
                          token t sit at [(step*T + t)*4 .. +3]                 */

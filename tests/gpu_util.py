@@ -79,6 +79,13 @@ def _check_packed(r):
     assert np.array_equal(cm[r["O"]], -(np.arange(k) + 1))
     if r["packed"].k_pad:
         assert np.array_equal(u8(v["B_q"]), pk["Bq"]), "B_q differs"
+        # the GEMM's tiled copy holds the same codes, and zeros past d_out
+        assert np.array_equal(u8(v["B_q_from_tiles"]), pk["Bq"]), "B_q_tiles differs"
+        rows16 = (pk["d_out"] + 15) // 16 * 16
+        if rows16 > pk["d_out"]:
+            from bit_quantized_dit_amd.w4a4 import untile_codes
+            full = untile_codes(v["B_q_tiles_raw"], rows16, pk["K_pad"])
+            assert not bool(full[pk["d_out"]:].any()), "B_q_tiles padding rows not zero"
         assert np.array_equal(u8(v["B_s"]), pk["Bs"]), "B_s differs"
         # the GEMM's step-major per-row copy holds the group code of every (row, 32-block)
         d_out, K_pad, lay = pk["d_out"], pk["K_pad"], pk["layout"]

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from bit_quantized_dit_amd import w4a4 as B
@@ -72,7 +73,7 @@ def _fake_desc(d_in=512, d_out=1024, k=16, layout=0):
     d.k_pad = (d.k_j + 127) // 128 * 128
     d.k_ld = (k + 31) // 32 * 32
     fake = 0x100000  # never dereferenced: only host-side logic runs below
-    d.colmap = d.s = d.O = d.J = d.B_q = d.B_s = d.B_s_rows = d.W_O = fake
+    d.colmap = d.s = d.O = d.J = d.B_q = d.B_s = d.B_s_rows = d.W_O = d.B_q_tiles = fake
     return d
 
 
@@ -82,6 +83,9 @@ def test_workspace_layout_is_host_logic(L):
     assert L.w4a4_workspace_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 0
     assert out.a_q == 0 and out.a_s >= 1000 * 256 and out.x_o >= out.a_s + 1000 * 16
     assert out.total >= out.x_o + 1000 * 32 * 2 and out.total % 256 == 0
+    # A_q is tiled in 16-token blocks: a ragged T reserves the whole last block
+    assert L.w4a4_workspace_layout(1001, ctypes.byref(d), ctypes.byref(out)) == 0
+    assert out.a_s >= 1008 * 256
     n = ctypes.c_size_t(0)
     assert L.w4a4_workspace_size(0, ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
 
@@ -116,3 +120,22 @@ def test_per_call_entry_points_validate_before_any_launch(L):
                                    ctypes.c_float(0.5), 65, ctypes.c_void_p(256), ctypes.c_void_p(256),
                                    None, None, None) == 1
     assert L.w4a4_gelu_tanh_bf16(ctypes.c_void_p(258), 8, ctypes.c_void_p(256), None) == 3
+
+
+def test_untile_codes_inverts_the_documented_tiled_order():
+    """The binding's de-tiling (used to compare the tiled A_q / B_q copies with the
+    oracle's row-major codes) inverts the order the header documents."""
+    import torch
+    rng = np.random.default_rng(5)
+    rows, k_pad = 48, 384
+    canon = rng.integers(0, 256, size=(rows, k_pad // 2), dtype=np.uint8)
+    nkb = k_pad // 128
+    tiled = np.zeros(rows * k_pad // 2, dtype=np.uint8)
+    for t in range(rows):
+        for byte in range(k_pad // 2):
+            p = 2 * byte
+            c = (p % 128) // 32
+            off = ((t // 16) * nkb + p // 128) * 1024 + (t % 16) * 64 + (c ^ ((t % 16) // 4)) * 16 + ((p % 128) // 2) % 16
+            tiled[off] = canon[t, byte]
+    got = B.untile_codes(torch.from_numpy(tiled), rows, k_pad).numpy()
+    assert np.array_equal(got, canon)
