@@ -82,6 +82,40 @@ def cpu_baseline(inp, s, O, layout, budget_s: float = 12.0):
                       f"{t:.1f} s"}
 
 
+def quality(inp, X, W, spec, s, O, act_scale, tokens: int = 512):
+    """Quantization error of the layer, reported without a gate: relative Frobenius
+    error of Y against the unquantized fp64 product X W^T on the first `tokens`
+    tokens, for naive W4A4 (s = 1, no outlier columns), smoothing only, the outlier
+    split only (s = 1, the top-k columns by raw activation maximum) and smoothing +
+    split (the method).  Every quantized Y comes from the library on the GPU."""
+    import torch
+
+    from bit_quantized_dit_amd import synth
+    from bit_quantized_dit_amd import w4a4 as B
+
+    Xh = X[:tokens]
+    Xf = inp["X"][:tokens]
+    Xf = synth.bf16_bits_to_f32(Xf) if Xf.dtype == np.uint16 else Xf
+    Yref = Xf.astype(np.float64) @ inp["W"].astype(np.float64).T
+    d_out, d_in = inp["W"].shape
+    ones = np.ones(d_in, np.float32)
+    none = np.zeros(0, np.int32)
+    O_raw = np.sort(np.argsort(-act_scale, kind="stable")[:spec.k]).astype(np.int32)
+    cases = {"naive_w4a4": (ones, none), "smooth_only": (s, none),
+             "split_only": (ones, O_raw), "smooth_split": (s, O)}
+    out = {}
+    for name, (s_c, O_c) in cases.items():
+        pk = B.w4a4_pack_weights(W, s_c, O_c, spec.layout)
+        ws = B.alloc_workspace(tokens, pk)
+        Y = torch.empty(tokens, d_out, dtype=torch.float32, device=X.device)
+        B.w4a4_linear(Xh, pk, Y, ws)
+        torch.cuda.synchronize()
+        out[name] = float(np.linalg.norm(Y.cpu().numpy().astype(np.float64) - Yref) / np.linalg.norm(Yref))
+    out["tokens"] = tokens
+    out["reference"] = "fp64 X W^T, unquantized"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +123,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quality", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run 4 plain device-to-device copies of this "
                          "many MiB (the known-size kernel that scales HBM byte counters)")
@@ -128,7 +163,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     X, Xc, W = to_dev(inp["X"]), to_dev(inp["X_cal"]), to_dev(inp["W"])
-    s, O, _, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, spec.k)
+    s, O, act_scale, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, spec.k)
     packed = B.w4a4_pack_weights(W, s, O, spec.layout)
     T, d_in, d_out, k = spec.T, spec.d_in, spec.d_out, spec.k
     ws = B.alloc_workspace(T, packed)
@@ -188,6 +223,10 @@ def main():
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_FP4_TFLOPS,
                      "traffic": traffic},
     }
+    if not args.no_quality:
+        log("[bench] quantization error report (ungated) ...")
+        result["quality"] = quality(inp, X, W, spec, s, O, act_scale)
+        log(f"[bench] quality {result['quality']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(inp, s, O, spec.layout)

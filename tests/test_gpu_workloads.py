@@ -139,3 +139,27 @@ def test_workload5_ffn_block(orc, mini):
     Ysel = Y[torch.as_tensor(drows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
     st = assert_y_close(Ysel.cpu().numpy(), Yref)
     _banner(f"  down: {st}")
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,layout", [(2600, 640, 7001, 24, 0), (2600, 640, 6912, 24, 1)])
+def test_many_tiles_per_workgroup_with_ragged_edges(orc, T, d_in, d_out, k, layout):
+    """More output tiles than the persistent grid has workgroups, so workgroups run
+    several tiles in a row, full and ragged ones (token tail, feature tail, and an
+    output width that is not a multiple of 4): every output row and column at a tile
+    edge is checked, plus random samples."""
+    spec = synth.WORKLOADS[2]
+    _banner(f"many tiles T={T} d_in={d_in} d_out={d_out} k={k} layout={layout}")
+    inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=256)
+    r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, k, layout)
+    _check_packed(r)
+    rng = np.random.default_rng(11)
+    Aq_o, As_o, XO_o = orc.act_prep(inp["X"], r["s"], r["O"], r["J"])
+    edge_t = np.array(sorted({0, 255, 256, 511, 512, T - 257, T - 256, T - 2, T - 1}))
+    edge_n = np.array(sorted({0, 255, 256, d_out - 257, d_out - 256, d_out - 4, d_out - 2, d_out - 1}))
+    ts = [np.repeat(edge_t, d_out), np.tile(np.arange(T), edge_n.size), rng.integers(0, T, 8192)]
+    ns = [np.tile(np.arange(d_out), edge_t.size), np.repeat(edge_n, T), rng.integers(0, d_out, 8192)]
+    ts, ns = np.concatenate(ts), np.concatenate(ns)
+    Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts, ns)
+    Ysel = r["Y"][torch.as_tensor(ts, device="cuda"), torch.as_tensor(ns, device="cuda")]
+    st = assert_y_close(Ysel.cpu().numpy(), Yref)
+    _banner(f"  {st} over {ts.size} outputs")
