@@ -5,11 +5,12 @@
 // One workgroup streams whole token rows (persistent over rows) through an LDS copy
 // laid out as [k_pad] J-compacted smoothed values followed by [k_ld] outlier values.
 //   phase 1  every column goes to its fixed LDS slot, no branches: J column j at its
-//            compacted position as fl32(x / s_j) (IEEE binary32 division), outlier
+//            compacted position as fl32(x / s_j) (the correctly rounded binary32
+//            quotient, from a double product with RN64(1 / s_j), see div_by_s), outlier
 //            column O[i] at k_pad + i as the raw x.  Lane i of the workgroup owns the
 //            column pairs 2(i + 512m), 2(i+512m)+1 (one 4-byte load for bf16, 8 bytes
 //            for fp32, so each wavefront load is one contiguous run) and keeps their
-//            slots and s in registers for the whole launch.
+//            slots and 1 / s_j in registers for the whole launch.
 //   phase 2  each thread takes 8 consecutive compacted positions (two 16-byte LDS
 //            reads); four lanes form one 32-block and meet their |x| maxima through two
 //            DPP quad permutes; the E8M0 code follows from the maximum's exponent field
@@ -97,6 +98,22 @@ __device__ __forceinline__ void copy_outliers(const float* row, int64_t k_pad, i
     for (int64_t i = threadIdx.x; i < k_ld; i += NT) xo_row[i] = bf16_rne(row[k_pad + i]);
 }
 
+// fl32(x / s) from r = RN64(1 / s): the double product x * r lies within 2^-52
+// (relative) of the exact quotient x / s (one rounding in r, one in the product),
+// while a quotient of two binary32 numbers is never a binary32 rounding boundary
+// (a midpoint between neighbours) and stays at least ~2^-49 (relative) away from
+// every such boundary: with x = X 2^a, s = S 2^b (X, S < 2^24) and a midpoint
+// M 2^c (M odd, 2^24 <= M < 2^25), x - M 2^c s is a nonzero multiple of the
+// smaller of 2^a and 2^(b+c), which bounds |x/s - M 2^c| / (x/s) below by
+// 1 / (S M) > 2^-49.  Rounding the double product to binary32 (nearest even, the
+// default mode; subnormal results kept) therefore yields the correctly rounded
+// binary32 quotient, signed zeros and infinities included (x = +-0 or +-Inf give
+// +-0 or +-Inf; a NaN stays a NaN, which only ever sets its group's scale to NaN).
+// Three VALU operations instead of the eleven of the IEEE binary32 divide.
+__device__ __forceinline__ float div_by_s(float x, double r) {
+    return (float)((double)x * r);
+}
+
 // Fixed LDS slot of input column j from its column-map entry.
 __device__ __forceinline__ int32_t slot_of(int32_t m, int64_t k_pad) {
     return m >= 0 ? m : (int32_t)k_pad + (-m - 1);
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     // batch's first wait; only the LDS writes of lanes past the last pair are skipped.
     const int64_t npairs = d_in / 2;
     int32_t slot[MAXM][2];
-    float sv[MAXM][2];
+    double rv[MAXM][2];   // RN64(1 / s_j) of the lane's columns
     bool outl[MAXM][2];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
@@ -179,8 +196,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
         const float2 s2 = reinterpret_cast<const float2*>(s)[pi];
         slot[m][0] = slot_of(cm.x, k_pad);
         slot[m][1] = slot_of(cm.y, k_pad);
-        sv[m][0] = s2.x;
-        sv[m][1] = s2.y;
+        rv[m][0] = 1.0 / (double)s2.x;
+        rv[m][1] = 1.0 / (double)s2.y;
         outl[m][0] = cm.x < 0;
         outl[m][1] = cm.y < 0;
     }
@@ -216,7 +233,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 const float lo = Pair<XT>::lo(xv[d][m]), hi = Pair<XT>::hi(xv[d][m]);
-                const float qlo = lo / sv[m][0], qhi = hi / sv[m][1];
+                const float qlo = div_by_s(lo, rv[m][0]), qhi = div_by_s(hi, rv[m][1]);
                 if ((int64_t)threadIdx.x + (int64_t)NT * m < npairs) {
                     row[slot[m][0]] = outl[m][0] ? lo : qlo;
                     row[slot[m][1]] = outl[m][1] ? hi : qhi;
