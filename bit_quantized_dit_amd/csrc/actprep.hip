@@ -32,15 +32,13 @@ namespace w4a4 {
 // fast path takes 1024 lanes up to d_in = 16384.
 constexpr int AP_THREADS = 512;
 
-// Rows per batch: within ~10 registers of row data per lane and per batch (one
-// register per bf16 pair, two per fp32 pair); two batches are live at once, and the
-// kernel stays within 128 VGPRs (four waves per SIMD: two 512-lane workgroups or one
-// 1024-lane workgroup per CU).
-template <typename XT, int MAXM>
-constexpr int ap_depth() {
-    constexpr int regs = MAXM * (int)(sizeof(XT) / 2);
-    return regs * 4 <= 10 ? 4 : regs * 3 <= 10 ? 3 : regs * 2 <= 10 ? 2 : 1;
-}
+
+// LDS word of compacted position p: 16 bytes of padding follow every 32 positions,
+// so that the 16-byte phase-2 reads of consecutive lanes (32 bytes apart) spread
+// over all banks.  The outlier slots follow the last padded block.
+__device__ __forceinline__ int32_t lds_pos(int64_t p) { return (int32_t)(p + ((p >> 5) << 2)); }
+__device__ __forceinline__ int32_t lds_outliers(int64_t k_pad) { return lds_pos(k_pad); }
+__host__ __device__ inline int64_t lds_words(int64_t k_pad, int64_t k_ld) { return k_pad + k_pad / 8 + k_ld; }
 
 // Maximum of v over the four lanes of this lane's quad (lanes 4q..4q+3).
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
@@ -75,8 +73,9 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
     const int r = (int)(t & 15);
     uint8_t* aq_blk = Aq + (((t >> 4) * (k_pad / 128)) << 10) + (r << 6);
     for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += NT * 8) {
-        const float4 a = *reinterpret_cast<const float4*>(row + p0);
-        const float4 b = *reinterpret_cast<const float4*>(row + p0 + 4);
+        const float* src = row + lds_pos(p0);
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t m = 0;
 #pragma unroll
@@ -92,10 +91,10 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
     }
 }
 
-// X_O row from the outlier slots row[k_pad, k_pad + k_ld) (slots >= k hold zero).
+// X_O row from the outlier slots (slots >= k hold zero).
 template <int NT>
 __device__ __forceinline__ void copy_outliers(const float* row, int64_t k_pad, int64_t k_ld, uint16_t* xo_row) {
-    for (int64_t i = threadIdx.x; i < k_ld; i += NT) xo_row[i] = bf16_rne(row[k_pad + i]);
+    for (int64_t i = threadIdx.x; i < k_ld; i += NT) xo_row[i] = bf16_rne(row[lds_outliers(k_pad) + i]);
 }
 
 // fl32(x / s) from r = RN64(1 / s): the double product x * r lies within 2^-52
@@ -116,15 +115,15 @@ __device__ __forceinline__ float div_by_s(float x, double r) {
 
 // Fixed LDS slot of input column j from its column-map entry.
 __device__ __forceinline__ int32_t slot_of(int32_t m, int64_t k_pad) {
-    return m >= 0 ? m : (int32_t)k_pad + (-m - 1);
+    return m >= 0 ? lds_pos(m) : lds_outliers(k_pad) + (-m - 1);
 }
 
 // Zero the parts of the LDS row that phase 1 never writes: the J tail [k_j, k_pad)
-// and the unused outlier slots [k_pad + k, k_pad + k_ld).
+// and the unused outlier slots k .. k_ld-1.
 template <int NT>
 __device__ __forceinline__ void zero_pads(float* row, int64_t k_j, int64_t k_pad, int32_t k, int64_t k_ld) {
-    for (int64_t p = k_j + threadIdx.x; p < k_pad; p += NT) row[p] = 0.0f;
-    for (int64_t p = k_pad + k + threadIdx.x; p < k_pad + k_ld; p += NT) row[p] = 0.0f;
+    for (int64_t p = k_j + threadIdx.x; p < k_pad; p += NT) row[lds_pos(p)] = 0.0f;
+    for (int64_t i = k + threadIdx.x; i < k_ld; i += NT) row[lds_outliers(k_pad) + i] = 0.0f;
 }
 
 template <typename XT>
@@ -156,24 +155,46 @@ __global__ __launch_bounds__(AP_THREADS) void actprep_kernel(
     }
 }
 
+// Two neighbouring elements of X (a 4-byte bf16 pair, an 8-byte fp32 pair) from a
+// buffer descriptor; out-of-range offsets read zero.
 template <typename XT>
 struct Pair;
 template <>
 struct Pair<uint16_t> {
     typedef uint32_t raw;
-    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
-    __device__ static float lo(raw r) { return __uint_as_float(r << 16); }
-    __device__ static float hi(raw r) { return __uint_as_float(r & 0xFFFF0000u); }
+    __device__ static raw load(__amdgpu_buffer_rsrc_t r, int32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    __device__ static float lo(raw v) { return __uint_as_float(v << 16); }
+    __device__ static float hi(raw v) { return __uint_as_float(v & 0xFFFF0000u); }
 };
 template <>
 struct Pair<float> {
-    typedef float2 raw;
-    __device__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
-    __device__ static float lo(raw r) { return r.x; }
-    __device__ static float hi(raw r) { return r.y; }
+    typedef uint2 raw;
+    __device__ static raw load(__amdgpu_buffer_rsrc_t r, int32_t off) {
+        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+        const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint2(v.x, v.y);
+    }
+    __device__ static float lo(raw v) { return __uint_as_float(v.x); }
+    __device__ static float hi(raw v) { return __uint_as_float(v.y); }
 };
 
-// Fast path: d_in even, X 8-byte aligned, d_in <= 2 * NT * MAXM.
+// Rows per batch: two batches are live at once; within ~10 registers of row data per
+// lane and batch (one register per bf16 pair, two per fp32 pair), so that the kernel
+// stays within 128 VGPRs (four waves per SIMD: two 512-lane workgroups or one
+// 1024-lane workgroup per CU).
+template <typename XT, int MAXM>
+constexpr int ap_depth() {
+    constexpr int regs = MAXM * (int)(sizeof(XT) / 2);
+    return regs * 4 <= 10 ? 4 : regs * 3 <= 10 ? 3 : regs * 2 <= 10 ? 2 : 1;
+}
+
+// Fast path: d_in even, d_in <= 2 * NT * MAXM.  Lane i owns the column pairs
+// 2(i + NT*m), 2(i + NT*m) + 1: one 4-byte (bf16) or 8-byte (fp32) load per pair, so
+// a wavefront's loads of one m are one contiguous run.  Rows are read through a
+// buffer descriptor per row (range d_in elements; zero range past the workgroup's
+// last row), so every load is unpredicated with a per-lane constant offset.
 template <typename XT, int NT, int MAXM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void actprep_pairs_kernel(
     const XT* __restrict__ X, int64_t T, int64_t d_in, const int32_t* __restrict__ colmap,
@@ -182,9 +203,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     extern __shared__ float row[];
     zero_pads<NT>(row, k_j, k_pad, k, k_ld);
 
-    // Loads are never predicated (lanes past the last pair re-read it, rows past T
-    // re-read row T-1) so that the compiler sees every load of a batch complete at the
-    // batch's first wait; only the LDS writes of lanes past the last pair are skipped.
     const int64_t npairs = d_in / 2;
     int32_t slot[MAXM][2];
     double rv[MAXM][2];   // RN64(1 / s_j) of the lane's columns
@@ -211,16 +229,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     const int64_t t_begin = (int64_t)blockIdx.x * per_wg;
     const int64_t t_end = min(T, t_begin + per_wg);
     if (t_begin >= t_end) return;
-    auto row_of = [&](int64_t r) __attribute__((always_inline)) { return t_begin + r; };
+    const int row_bytes = (int)(d_in * (int64_t)sizeof(XT));
     auto fetch = [&](raw (*xv)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const XT* xr = X + min(row_of(r0 + d), t_end - 1) * d_in;
+            const int64_t t = t_begin + r0 + d;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(X + (t < t_end ? t : t_begin) * d_in), 0, t < t_end ? row_bytes : 0, 0x00020000);
 #pragma unroll
-            for (int m = 0; m < MAXM; ++m) {
-                const int64_t pi = min((int64_t)threadIdx.x + (int64_t)NT * m, npairs - 1);
-                xv[d][m] = Pair<XT>::load(xr + 2 * pi);
-            }
+            for (int m = 0; m < MAXM; ++m)
+                xv[d][m] = Pair<XT>::load(rs, (int32_t)((threadIdx.x + NT * m) * 2 * sizeof(XT)));
         }
     };
     // Rows r0 .. r0+D-1 of this workgroup from xv; the loads of the next batch into
@@ -228,7 +246,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     auto batch = [&](raw (*xv)[MAXM], raw (*xn)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t t = row_of(r0 + d);
+            const int64_t t = t_begin + r0 + d;
             if (t >= t_end) break;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
@@ -248,9 +266,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     };
     raw xa[D][MAXM], xb[D][MAXM];
     fetch(xa, 0);
-    for (int64_t r = 0; row_of(r) < t_end; r += 2 * D) {
+    for (int64_t r = 0; t_begin + r < t_end; r += 2 * D) {
         batch(xa, xb, r);
-        if (row_of(r + D) >= t_end) break;
+        if (t_begin + r + D >= t_end) break;
         batch(xb, xa, r + D);
     }
 }
@@ -258,11 +276,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
 template <typename XT>
 static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uint8_t* Aq, uint8_t* As,
                                uint16_t* XO, hipStream_t st) {
-    const size_t lds = (size_t)(d.k_pad + d.k_ld > 0 ? d.k_pad + d.k_ld : 1) * sizeof(float);
+    const size_t lds = (size_t)(lds_words(d.k_pad, d.k_ld) > 0 ? lds_words(d.k_pad, d.k_ld) : 1) * sizeof(float);
     const int64_t grid64 = T < 2048 ? T : 2048;
     const unsigned grid = (unsigned)grid64;
-    const bool pairs = (d.d_in % 2 == 0) && (((uintptr_t)X & 7u) == 0);
-    const int64_t npairs = d.d_in / 2;
+    const int64_t n = d.d_in;
 #define W4A4_AP_LAUNCH(KERNEL, NT)                                                                   \
     {                                                                                                \
         if (lds > 65536) {                                                                           \
@@ -275,7 +292,7 @@ static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uin
         return hipGetLastError();                                                                    \
     }
 #define W4A4_AP_PAIRS(NT, M) \
-    if (pairs && npairs <= (int64_t)(NT) * (M)) W4A4_AP_LAUNCH((actprep_pairs_kernel<XT, NT, M>), NT)
+    if (n % 2 == 0 && n <= 2 * (int64_t)(NT) * (M)) W4A4_AP_LAUNCH((actprep_pairs_kernel<XT, NT, M>), NT)
     W4A4_AP_PAIRS(512, 1)
     W4A4_AP_PAIRS(512, 2)
     W4A4_AP_PAIRS(512, 3)
