@@ -25,8 +25,8 @@
 // Tiling: a 512-thread workgroup (8 wavefronts, 2 token halves x 4 feature quarters,
 // two per SIMD) owns a 256-token x 256-feature output tile; each wavefront a
 // 128 x 64 sub-tile (4 x 2 MFMA tiles, 128 fp32 accumulators per lane in AGPRs), so
-// that one wavefront's LDS waits, barrier waits and epilogue stores are covered by
-// the MFMAs of its SIMD partner.  The 256 x 256 tile keeps the global traffic per
+// that one wavefront's LDS waits and barrier waits are covered by the MFMAs of its
+// SIMD partner.  The 256 x 256 tile keeps the global traffic per
 // MFMA at the level that the per-CU vector memory path sustains.  The K loop walks 128-code steps
 // (64 bytes per row).  Operands move HBM/L2 -> LDS with buffer_load ... lds (no
 // VGPR staging) into a ring of STAGES slots; STAGES-1 steps are in flight while the
@@ -389,27 +389,45 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // ---- epilogue: lane holds token l32 and features 8q + 4*lh + r of each tile
+    // ---- epilogue.  Lane l holds token l32 and features 8q + 4*lh + r of each MFMA
+    // tile; the wavefront restages each 32-token slab of its 128 x 64 sub-tile through
+    // LDS (the ring is idle now) so that every store instruction writes 4 whole rows
+    // of 64 features (256 contiguous bytes each) instead of 32 rows x 32 bytes.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+        constexpr int SROW = 64 + 4;   // staged row stride in floats (16 bytes of padding)
+        static_assert((G_THREADS / 64) * 32 * SROW * 4 <= STAGES * SLOT_BYTES, "staging fits the ring");
+        float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SROW);
+        const bool full = (T - t0 >= BT) && (N - f0 >= BF) && vec_store;
 #pragma unroll
-    for (int j = 0; j < FT; ++j) {
-        const int64_t t = t0 + wt * 128 + j * 32 + l32;
-        if (t >= T) continue;
+        for (int j = 0; j < FT; ++j) {
 #pragma unroll
-        for (int i = 0; i < FF; ++i) {
+            for (int i = 0; i < FF; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = f0 + wf * 64 + i * 32 + 8 * q + 4 * lh;
-                float* dst = Y + t * N + n;
-                const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                  acc[i][j][4 * q + 3]};
-                if (vec_store && n + 3 < N) {
-                    *reinterpret_cast<v4f*>(dst) = v;
-                } else {
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f*>(stage + l32 * SROW + i * 32 + 8 * q + 4 * lh) =
+                        v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N) dst[r] = v[r];
+            for (int k = 0; k < 8; ++k) {
+                const int r = (lane >> 4) + 4 * k;
+                const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
+                const int64_t t = t0 + wt * 128 + j * 32 + r;
+                const int64_t n = f0 + wf * 64 + (lane & 15) * 4;
+                if (full) {
+                    *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                } else if (t < T) {
+                    if (vec_store && n + 3 < N) {
+                        *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) Y[t * N + n + e] = v[e];
+                    }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slab read before the next overwrites it
         }
     }
 }
