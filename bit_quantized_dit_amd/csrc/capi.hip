@@ -258,32 +258,60 @@ int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_
                                      (hipStream_t)stream));
 }
 
-int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+int gemm_into(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, void* out, bool gelu,
+              void* stream) {
     if (T < 0) return W4A4_ERR_INVALID;
     int st = check_desc(desc);
     if (st) return st;
     if (T == 0) return W4A4_OK;
-    if (!ws || !Y) return W4A4_ERR_INVALID;
-    if (misaligned(ws) || misaligned(Y)) return W4A4_ERR_ALIGN;
+    if (!ws || !out) return W4A4_ERR_INVALID;
+    if (misaligned(ws) || misaligned(out)) return W4A4_ERR_ALIGN;
     const w4a4_ws_layout w = ws_layout(T, desc);
     if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
     const uint8_t* b = (const uint8_t*)ws;
-    return dev_status(launch_gemm(b + w.a_q, b + w.a_s, (const uint16_t*)(b + w.x_o), T, *desc, Y,
+    return dev_status(launch_gemm(b + w.a_q, b + w.a_s, (const uint16_t*)(b + w.x_o), T, *desc, out, gelu,
                                   (hipStream_t)stream));
+}
+
+int linear_into(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, void* out, bool gelu,
+                void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    int st = check_desc(desc);
+    if (st) return st;
+    if (T == 0) return W4A4_OK;
+    if (!out) return W4A4_ERR_INVALID;
+    if (misaligned(out)) return W4A4_ERR_ALIGN;
+    st = w4a4_quantize_activations(X, x_dtype, T, desc, ws, ws_bytes, stream);
+    if (st) return st;
+    return gemm_into(ws, ws_bytes, T, desc, out, gelu, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
+                           void* stream) {
+    return gemm_into(ws, ws_bytes, T, desc, Y, false, stream);
+}
+
+int w4a4_gemm_prequantized_gelu_bf16(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
+                                     uint16_t* H, void* stream) {
+    return gemm_into(ws, ws_bytes, T, desc, H, true, stream);
 }
 
 int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y, void* ws,
                 size_t ws_bytes, void* stream) {
-    if (T < 0) return W4A4_ERR_INVALID;
-    int st = check_desc(desc);
-    if (st) return st;
-    if (T == 0) return W4A4_OK;
-    if (!Y) return W4A4_ERR_INVALID;
-    if (misaligned(Y)) return W4A4_ERR_ALIGN;
-    st = w4a4_quantize_activations(X, x_dtype, T, desc, ws, ws_bytes, stream);
-    if (st) return st;
-    return w4a4_gemm_prequantized(ws, ws_bytes, T, desc, Y, stream);
+    return linear_into(X, x_dtype, T, desc, Y, false, ws, ws_bytes, stream);
+}
+
+int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, uint16_t* H,
+                          void* ws, size_t ws_bytes, void* stream) {
+    return linear_into(X, x_dtype, T, desc, H, true, ws, ws_bytes, stream);
 }
 
 int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream) {

@@ -129,11 +129,18 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nt_m, int64_t nt_n,
     tn = in_g / gsize;
 }
 
+// GELU = false: out is fp32 Y [T][N].  GELU = true: out is bf16 H [T][N] with
+// H = bf16(gelu_tanh(bf16(Y))) applied to each fp32 output in the epilogue (the FFN
+// up projection feeding the down projection, sec. 3.1 / 3.5), bit-identical to the
+// standalone GELU pass over this kernel's Y.
+template <bool GELU>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As, const uint16_t* __restrict__ XO,
     int64_t T, const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs_rows,
-    const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, float* __restrict__ Y,
+    const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, void* __restrict__ out,
     int vec_store) {
+    float* __restrict__ Y = reinterpret_cast<float*>(out);
+    uint16_t* __restrict__ H = reinterpret_cast<uint16_t*>(out);
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * SLOT_BYTES];
 
     const int tid = threadIdx.x;
@@ -415,15 +422,32 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                 const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
                 const int64_t t = t0 + wt * 128 + j * 32 + r;
                 const int64_t n = f0 + wf * 64 + (lane & 15) * 4;
-                if (full) {
-                    *reinterpret_cast<v4f*>(Y + t * N + n) = v;
-                } else if (t < T) {
-                    if (vec_store && n + 3 < N) {
-                        *reinterpret_cast<v4f*>(Y + t * N + n) = v;
-                    } else {
+                if constexpr (GELU) {
+                    const uint32_t h0 = gelu_tanh_bf16(v[0]), h1 = gelu_tanh_bf16(v[1]);
+                    const uint32_t h2 = gelu_tanh_bf16(v[2]), h3 = gelu_tanh_bf16(v[3]);
+                    if (full) {
+                        *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    } else if (t < T) {
+                        if (vec_store && n + 3 < N) {
+                            *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                        } else {
+                            const uint32_t hv[4] = {h0, h1, h2, h3};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) Y[t * N + n + e] = v[e];
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N) H[t * N + n + e] = (uint16_t)hv[e];
+                        }
+                    }
+                } else {
+                    if (full) {
+                        *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                    } else if (t < T) {
+                        if (vec_store && n + 3 < N) {
+                            *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N) Y[t * N + n + e] = v[e];
+                        }
                     }
                 }
             }
@@ -433,15 +457,20 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
 }
 
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                       const w4a4_packed& d, float* Y, hipStream_t st) {
+                       const w4a4_packed& d, void* out, bool gelu_bf16, hipStream_t st) {
     if (T <= 0 || d.d_out <= 0) return hipSuccess;
     const int64_t tiles = ((T + BT - 1) / BT) * ((d.d_out + BF - 1) / BF);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     // 32-bit buffer offsets: one tile's rows of codes must span < 2 GiB
     if ((int64_t)BT * (d.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)Y & 15u) == 0);
-    gemm_w4a4_kernel<<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
-        Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, Y, vec_store);
+    // vector stores: 16 bytes (fp32) or 8 bytes (bf16) per lane, aligned when every row is
+    const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)out & 15u) == 0);
+    if (gelu_bf16)
+        gemm_w4a4_kernel<true><<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
+            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
+    else
+        gemm_w4a4_kernel<false><<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
+            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
     return hipGetLastError();
 }
 

@@ -46,13 +46,33 @@ __device__ __forceinline__ uint32_t e2m1_nibble(float x, float inv) {
     return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// binary32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// binary32 -> bf16, round to nearest even; a NaN becomes the canonical quiet NaN
+// with its sign kept.
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// GELU-tanh between the FFN projections ("W4A4 Quantization for Inference on
+// Wan2.2-I2V-A14B (ICME 2026 Challenge)", sec. 3.1 and 3.5) on one fp32 output:
+// bf16(gelu_tanh(bf16(y))), gelu_tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))),
+// evaluated as x / (1 + exp(-2z)), z = sqrt(2/pi)(x + 0.044715 x^3): the same function
+// (0.5(1 + tanh z) is the logistic of 2z) without the cancellation in 1 + tanh z that
+// wipes out every digit of the negative tail in binary32.  exp and the reciprocal are
+// the hardware v_exp_f32 (2^t) and v_rcp_f32, each within about one binary32 ulp, so
+// the fp32 value is within a few ulps of the exact function before the final rounding
+// to bf16 (8 significant bits).  Tails: x -> -inf gives exp -> inf, rcp -> 0 and a
+// signed zero; x -> +inf gives x.  Shared by the standalone GELU kernel and the GEMM
+// epilogue that fuses it, so both give the same bits.
+__device__ __forceinline__ uint16_t gelu_tanh_bf16(float y) {
+    const float x = bf16_to_f32(bf16_rne(y));
+    const float c = 0.7978845608028654f;           // sqrt(2/pi)
+    const float z = c * (x + 0.044715f * x * x * x);
+    const float e = __builtin_amdgcn_exp2f(z * -2.8853900817779268f);   // exp(-2z) = 2^(-2 log2(e) z)
+    return bf16_rne(x * __builtin_amdgcn_rcpf(1.0f + e));
+}
 
 }  // namespace w4a4

@@ -16,8 +16,9 @@ hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st);
 hipError_t launch_actprep(const void* X, int x_dtype, int64_t T, const w4a4_packed& d,
                           uint8_t* Aq, uint8_t* As, uint16_t* XO, hipStream_t st);
 
+// out: fp32 Y [T][d_out], or bf16 H = bf16(gelu_tanh(bf16(Y))) when gelu_bf16
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                       const w4a4_packed& d, float* Y, hipStream_t st);
+                       const w4a4_packed& d, void* out, bool gelu_bf16, hipStream_t st);
 
 hipError_t launch_gelu(const float* Y, int64_t n, uint16_t* H, hipStream_t st);
 

@@ -28,7 +28,7 @@ STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR
 EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", "w4a4_packed_size",
            "w4a4_pack_weights", "w4a4_workspace_layout", "w4a4_workspace_size",
            "w4a4_quantize_activations", "w4a4_gemm_prequantized", "w4a4_linear",
-           "w4a4_gelu_tanh_bf16")
+           "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16")
 
 
 class W4A4Packed(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_quantize_activations": (ci, [vp, ci, i64, P(W4A4Packed), vp, sz, vp]),
             "w4a4_gemm_prequantized": (ci, [vp, sz, i64, P(W4A4Packed), vp, vp]),
             "w4a4_linear": (ci, [vp, ci, i64, P(W4A4Packed), vp, vp, sz, vp]),
+            "w4a4_gemm_prequantized_gelu_bf16": (ci, [vp, sz, i64, P(W4A4Packed), vp, vp]),
+            "w4a4_linear_gelu_bf16": (ci, [vp, ci, i64, P(W4A4Packed), vp, vp, sz, vp]),
             "w4a4_gelu_tanh_bf16": (ci, [vp, i64, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -305,6 +307,28 @@ def w4a4_linear(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, ws: torch
     st = lib().w4a4_linear(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
                            ws.numel(), _stream(stream))
     _check("w4a4_linear", st)
+
+
+def w4a4_gemm_prequantized_gelu_bf16(ws: torch.Tensor, T: int, packed: PackedLayer, H: torch.Tensor,
+                                     stream=None) -> None:
+    _dev(H, "H")
+    if H.dtype != torch.bfloat16:
+        raise TypeError("H must be bfloat16")
+    st = lib().w4a4_gemm_prequantized_gelu_bf16(_ptr(ws), ws.numel(), T, ctypes.byref(packed.desc), _ptr(H),
+                                                _stream(stream))
+    _check("w4a4_gemm_prequantized_gelu_bf16", st)
+
+
+def w4a4_linear_gelu_bf16(X: torch.Tensor, packed: PackedLayer, H: torch.Tensor, ws: torch.Tensor,
+                          stream=None) -> None:
+    _dev(X, "X")
+    _dev(H, "H")
+    if H.dtype != torch.bfloat16:
+        raise TypeError("H must be bfloat16")
+    T = X.shape[0]
+    st = lib().w4a4_linear_gelu_bf16(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(H), _ptr(ws),
+                                      ws.numel(), _stream(stream))
+    _check("w4a4_linear_gelu_bf16", st)
 
 
 def w4a4_gelu_tanh_bf16(Y: torch.Tensor, H: torch.Tensor, stream=None) -> None:

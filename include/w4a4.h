@@ -175,6 +175,17 @@ int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a
 int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* The FFN up projection with its activation fused (sec. 3.1 / 3.5: ffn.0 is followed
+ * by GELU-tanh, whose bf16 output feeds ffn.2): the dual-branch GEMM of
+ * w4a4_gemm_prequantized / w4a4_linear, with every fp32 output y stored as
+ * H = bf16_rne(gelu_tanh(bf16_rne(y))) -- bit-identical to w4a4_gelu_tanh_bf16 over
+ * the fp32 Y of the unfused call, without writing or re-reading Y.
+ * H device bf16 [T][d_out] (16-byte aligned).  Async; never allocate. */
+int w4a4_gemm_prequantized_gelu_bf16(const void* ws, size_t ws_bytes, int64_t T,
+                                     const w4a4_packed* desc, uint16_t* H, void* stream);
+int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc,
+                          uint16_t* H, void* ws, size_t ws_bytes, void* stream);
+
 /* GELU-tanh between the FFN up (ffn.0) and down (ffn.2) projections named in
  * sec. 3.1 / 3.5: H = bf16_rne(gelu_tanh(bf16_rne(Y))), gelu_tanh(x) =
  * 0.5x(1+tanh(sqrt(2/pi)(x+0.044715x^3))) in fp32.  Y device fp32 [n], H device

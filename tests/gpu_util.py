@@ -32,7 +32,10 @@ def assert_y_close(Y: np.ndarray, Yref: np.ndarray, what: str = "Y") -> dict:
     Yref = np.asarray(Yref, dtype=np.float64)
     nan_ref = np.isnan(Yref)
     assert np.array_equal(np.isnan(Y), nan_ref), f"{what}: NaN pattern differs"
-    fin = ~nan_ref
+    inf_ref = np.isinf(Yref)
+    assert np.array_equal(Y[inf_ref], Yref[inf_ref]) and not np.isinf(Y[~inf_ref]).any(), \
+        f"{what}: infinities differ"
+    fin = ~nan_ref & ~inf_ref
     d = np.abs(Y[fin] - Yref[fin])
     scale = np.abs(Yref[fin]).max() if fin.any() else 0.0
     max_rel = float(d.max() / scale) if d.size and scale > 0 else float(d.max() if d.size else 0.0)

@@ -120,6 +120,18 @@ def test_per_call_entry_points_validate_before_any_launch(L):
                                    ctypes.c_float(0.5), 65, ctypes.c_void_p(256), ctypes.c_void_p(256),
                                    None, None, None) == 1
     assert L.w4a4_gelu_tanh_bf16(ctypes.c_void_p(258), 8, ctypes.c_void_p(256), None) == 3
+    # the fused up projection + GELU entry points validate the same way
+    assert L.w4a4_linear_gelu_bf16(ctypes.c_void_p(16), 0, -1, ctypes.byref(d), ctypes.c_void_p(16),
+                                   ctypes.c_void_p(16), 1 << 30, None) == 1
+    assert L.w4a4_linear_gelu_bf16(ctypes.c_void_p(256), 0, 4, ctypes.byref(d), None,
+                                   ctypes.c_void_p(256), 1 << 30, None) == 1
+    assert L.w4a4_linear_gelu_bf16(None, 0, 0, ctypes.byref(d), None, None, 0, None) == 0
+    assert L.w4a4_gemm_prequantized_gelu_bf16(ctypes.c_void_p(256), 10, 4, ctypes.byref(d),
+                                              ctypes.c_void_p(256), None) == 2
+    assert L.w4a4_gemm_prequantized_gelu_bf16(ctypes.c_void_p(256), 1 << 30, 4, ctypes.byref(d),
+                                              ctypes.c_void_p(264), None) == 3
+    assert L.w4a4_gemm_prequantized_gelu_bf16(ctypes.c_void_p(256), 1 << 30, 4, ctypes.byref(bad),
+                                              ctypes.c_void_p(256), None) == 1
 
 
 def test_untile_codes_inverts_the_documented_tiled_order():

@@ -98,6 +98,8 @@ def test_special_values(orc):
     X[7, :] = np.array([0x1], np.uint32).view(np.float32)[0]
     X[8, :] = np.float32(3.0) * np.float32(2.5)  # divides to the tie 2.5 when s = 3
     X[8, 0] = np.float32(21.0)
+    X[9, 3] = np.array([0xFFA5A5A5], np.uint32).view(np.float32)[0]   # NaN with payload, outlier column
+    X[10, 77] = -np.inf                                                # -Inf, outlier column
     s = np.full(d_in, 3.0, np.float32)
     s[::7] = np.float32(0.37)
     W = (rng.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)
@@ -138,6 +140,70 @@ def test_division_exhaustive_sample(orc):
     torch.cuda.synchronize()
     r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "T": T}
     _check_act(orc, r, X)
+
+
+def test_e2m1_threshold_neighbourhoods(orc):
+    """Every binary32 pattern within 4096 ulps of each E2M1 rounding threshold
+    {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} * 2^E and of the saturation region
+    {6, 8 - ulp} * 2^E, both signs, for block exponents E = -127 (the subnormal
+    scale), -126, -20, 0, 60 and 125: each 32-block holds one element that pins E
+    (1.5 * 2^(E+2)) and 31 swept values, with s = 1 so the codes are the quantizer
+    alone.  Codes and scales must match the oracle bit for bit."""
+    _banner("E2M1 threshold neighbourhoods")
+    thr = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.999999], np.float64)
+    vals = []
+    for E in (-127, -126, -20, 0, 60, 125):
+        for t in thr:
+            c = (np.float64(t) * np.float64(2.0) ** E)
+            if c < np.finfo(np.float32).tiny / 2 ** 23 or c > np.finfo(np.float32).max:
+                continue
+            centre = np.array([c], np.float32).view(np.int32)[0]
+            pats = (centre + np.arange(-4096, 4097, dtype=np.int64)).clip(1, 0x7F7FFFFF).astype(np.uint32)
+            v = pats.view(np.float32)
+            pin = np.float32(1.5 * 2.0 ** (E + 2))           # floor(log2) = E + 2 pins E
+            v = v[np.abs(v.astype(np.float64)) < 2.0 ** (E + 3)]   # in-group: |v| < 2^(E+3)
+            v = v[:(v.size // 31) * 31].reshape(-1, 31)
+            blocks = np.concatenate([np.full((v.shape[0], 1), pin, np.float32), v], axis=1)
+            neg = -blocks
+            vals.append(blocks)
+            vals.append(neg)
+    X = np.concatenate(vals).reshape(-1)
+    d_in = 1024
+    X = np.concatenate([X, np.zeros((-X.size) % d_in, np.float32)]).reshape(-1, d_in)
+    s = np.ones(d_in, np.float32)
+    O = np.zeros(0, np.int32)
+    J = np.arange(d_in, dtype=np.int32)
+    W = np.ones((32, d_in), np.float32) * 0.01
+    packed = B.w4a4_pack_weights(to_dev(W), s, O, 0)
+    T = X.shape[0]
+    ws = B.alloc_workspace(T, packed)
+    B.w4a4_quantize_activations(to_dev(X), packed, ws)
+    torch.cuda.synchronize()
+    r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "T": T}
+    _check_act(orc, r, X)
+    _banner(f"  {X.size} elements in {T} rows")
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,layout,dt", [(300, 700, 203, 13, 0, "f32"), (520, 1000, 512, 40, 2, "bf16")])
+def test_fused_gelu_matches_unfused(orc, T, d_in, d_out, k, layout, dt):
+    """w4a4_linear_gelu_bf16 writes exactly w4a4_gelu_tanh_bf16(w4a4_linear(X)), on a
+    ragged tile grid and (203 outputs) the unvectorised store path."""
+    _banner(f"fused GELU T={T} d_in={d_in} d_out={d_out}")
+    spec = synth.WORKLOADS[1]
+    inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=128)
+    X = inp["X"] if dt == "f32" else synth.to_bf16_bits(inp["X"])
+    Xd, Xcd, Wd = to_dev(X), to_dev(inp["X_cal"]), to_dev(inp["W"])
+    s, O, _, _ = B.w4a4_calibrate_scales(Xcd, Wd, spec.alpha, k)
+    packed = B.w4a4_pack_weights(Wd, s, O, layout)
+    ws = B.alloc_workspace(T, packed)
+    Y = torch.empty(T, d_out, dtype=torch.float32, device="cuda")
+    B.w4a4_linear(Xd, packed, Y, ws)
+    H = torch.empty(T, d_out, dtype=torch.bfloat16, device="cuda")
+    B.w4a4_gelu_tanh_bf16(Y, H)
+    Hf = torch.full((T, d_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.w4a4_linear_gelu_bf16(Xd, packed, Hf, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(Hf.view(torch.int16), H.view(torch.int16)))
 
 
 def test_column_absmax_bits(orc):

@@ -107,6 +107,13 @@ def test_workload5_ffn_block(orc, mini):
     _banner(f"  gelu: {mism} of {int(big.sum())} sampled elements differ by one bf16 ulp")
     assert mism <= big.sum() // 1000
     assert np.all(np.abs(a[~big]) <= 2e-6)
+    # the fused up projection (GELU in the GEMM epilogue) gives the same H bit for bit
+    H_fused = torch.empty_like(H)
+    B.w4a4_gemm_prequantized_gelu_bf16(r_up["ws"], T, r_up["packed"], H_fused)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(H_fused.view(torch.int16), H.view(torch.int16))), "fused GELU output differs"
+    _banner("  fused up+GELU: H identical to GELU(Y_up)")
+    del H_fused
     # down layer: calibrated on the bf16 GELU of the unquantized up projection of the
     # calibration tokens; run on the GPU's H
     del r_up["ws"]
