@@ -277,9 +277,20 @@ template <typename XT>
 static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uint8_t* Aq, uint8_t* As,
                                uint16_t* XO, hipStream_t st) {
     const size_t lds = (size_t)(lds_words(d.k_pad, d.k_ld) > 0 ? lds_words(d.k_pad, d.k_ld) : 1) * sizeof(float);
-    const int64_t grid64 = T < 2048 ? T : 2048;
-    const unsigned grid = (unsigned)grid64;
     const int64_t n = d.d_in;
+    // The fast paths run persistent workgroups, each over a contiguous token range:
+    // as many as are resident at once (two 512-lane or one 1024-lane workgroup per CU),
+    // so each pays its per-column setup (column map, 1/s) once for many rows.
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev] = c;
+    }
+    const int64_t resident = (n <= 2 * (int64_t)AP_THREADS * 8) ? 2 * (int64_t)cus[dev] : (int64_t)cus[dev];
+    const unsigned grid = (unsigned)(T < resident ? T : resident);
 #define W4A4_AP_LAUNCH(KERNEL, NT)                                                                   \
     {                                                                                                \
         if (lds > 65536) {                                                                           \
