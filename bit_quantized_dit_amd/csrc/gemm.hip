@@ -133,6 +133,13 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nt_m, int64_t nt_n,
 // H = bf16(gelu_tanh(bf16(Y))) applied to each fp32 output in the epilogue (the FFN
 // up projection feeding the down projection, sec. 3.1 / 3.5), bit-identical to the
 // standalone GELU pass over this kernel's Y.
+//
+// Persistent: workgroup b walks the tiles b, b + G, b + 2G, ... of the grouped order
+// (G = grid size, one workgroup per CU; b and b + G sit on the same XCD), and its ring
+// of LDS slots runs on across tile boundaries: the last steps of one tile already
+// fetch the first steps of the next, whose operands are then in flight while this
+// tile's last MFMAs and its epilogue run.  The refill that the last step would issue
+// waits until the epilogue, which restages the accumulators through that free slot.
 template <bool GELU>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As, const uint16_t* __restrict__ XO,
@@ -141,319 +148,419 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     int vec_store) {
     float* __restrict__ Y = reinterpret_cast<float*>(out);
     uint16_t* __restrict__ H = reinterpret_cast<uint16_t*>(out);
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * SLOT_BYTES];
+    // the ring, then 1 KiB per wavefront that only the null loads of a tile's last
+    // step write (never read)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * SLOT_BYTES + (G_THREADS / 64) * 1024];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wt = wave & 1;     // token half of the tile
     const int wf = wave >> 1;    // feature quarter of the tile
-    const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
-    int64_t tm, tn;
-    tile_of(blockIdx.x, nt_m, nt_n, tm, tn);
-    const int64_t t0 = tm * BT;
-    const int64_t f0 = tn * BF;
     const int l32 = lane & 31;
     const int lh = lane >> 5;    // which 32-code half of a 64-code MFMA step this lane feeds
-
-    v16f acc[FF][FT];
-#pragma unroll
-    for (int i = 0; i < FF; ++i)
-#pragma unroll
-        for (int j = 0; j < FT; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
+    const int64_t ntiles = nt_m * nt_n;
+    int64_t id = blockIdx.x;
+    if (id >= ntiles) return;
 
     const int64_t o_ld = k_ld * 2;       // bytes per row of X_O / W_O
     const int nkb = (int)(k_pad / 128);  // FP4 steps (128 codes = 64 bytes per row)
     const int nbf = (int)(k_ld / 32);    // BF16 steps (32 values = 64 bytes per row)
     const int nsteps = nkb + nbf;
+    // Ring steps per tile: at least STAGES, so that the prefetch never reaches past the
+    // next tile; the extra steps read null descriptors (zeros) and add nothing.
+    const int ns = nsteps > STAGES ? nsteps : STAGES;
 
-    if (nsteps > 0) {
-        const int64_t rows_a = T - t0 < BT ? T - t0 : BT;
-        const int64_t rows_b = N - f0 < BF ? N - f0 : BF;
-        // FP4 codes in the tiled order (1 KiB per 16-row block and step, the LDS
-        // swizzle already applied): a tile's 16 row blocks start blk bytes apart.
-        const int64_t blk = (int64_t)nkb * 1024;
-        const v4i srdA = make_srd(Aq + (t0 / 16) * blk, (uint32_t)((rows_a + 15) / 16 * blk));
-        const v4i srdB = make_srd(Bq + (f0 / 16) * blk, (uint32_t)((rows_b + 15) / 16 * blk));
-        // Step-major scales: step st's words of this tile's rows start at
-        // (st * rows_total + row0) * 4.  The step offset goes into the descriptor base
-        // (not soffset, which the range check does not cover), so the descriptor spans
-        // exactly the tile's valid rows and tail rows read zero.
-        auto scale_srd = [&](const uint8_t* base, int st, int64_t total, int64_t row0, int64_t rows)
-            __attribute__((always_inline)) {
-            return make_srd(base + ((int64_t)st * total + row0) * 4, (uint32_t)(rows * 4));
-        };
-        const v4i srdXO = make_srd(XO + t0 * k_ld, (uint32_t)(rows_a * o_ld));
-        const v4i srdWO = make_srd(WO + f0 * k_ld, (uint32_t)(rows_b * o_ld));
-        const v4i srd0 = make_srd(Aq, 0u);
-        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-        // per-lane source offsets of this wavefront's two 1 KiB row blocks per operand:
-        // block b covers rows 16b..16b+15 and lands at LDS b*1024 as it lies in memory
-        // for the FP4 codes (lane -> 16 contiguous bytes); the row-major bf16 outlier
-        // operands are gathered into the same order: lane -> row 16b + lane/4, physical
-        // chunk lane%4, logical chunk = physical ^ ((row >> 2) & 3)
-        int voff[2], voffo[2];
+    struct Tile {
+        int64_t t0, f0;
+        bool valid;
+    };
+    auto tile_at = [&](int64_t i) __attribute__((always_inline)) {
+        Tile t;
+        t.valid = i < ntiles;
+        int64_t tm = 0, tn = 0;
+        if (t.valid) tile_of(i, nt_m, nt_n, tm, tn);
+        t.t0 = tm * BT;
+        t.f0 = tn * BF;
+        return t;
+    };
+    auto rows_a_of = [&](const Tile& t) __attribute__((always_inline)) { return T - t.t0 < BT ? T - t.t0 : (int64_t)BT; };
+    auto rows_b_of = [&](const Tile& t) __attribute__((always_inline)) { return N - t.f0 < BF ? N - t.f0 : (int64_t)BF; };
+
+    // FP4 codes in the tiled order (1 KiB per 16-row block and step, the LDS swizzle
+    // already applied): a tile's 16 row blocks start blk bytes apart.  Step-major
+    // scales: step st's words of a tile's rows start at (st * rows_total + row0) * 4;
+    // the step offset goes into the descriptor base (not soffset, which the range check
+    // does not cover), so every descriptor spans exactly the tile's valid rows and tail
+    // rows read zero.
+    const int64_t blk = (int64_t)nkb * 1024;
+    const v4i srd0 = make_srd(Aq, 0u);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    // per-lane source offsets of this wavefront's two 1 KiB row blocks per operand:
+    // block b covers rows 16b..16b+15 and lands at LDS b*1024 as it lies in memory
+    // for the FP4 codes (lane -> 16 contiguous bytes); the row-major bf16 outlier
+    // operands are gathered into the same order: lane -> row 16b + lane/4, physical
+    // chunk lane%4, logical chunk = physical ^ ((row >> 2) & 3)
+    int voff[2], voffo[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 16 * (wave * 2 + h) + (lane >> 2);
-            const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
-            voff[h] = (wave * 2 + h) * (int)blk + lane * 16;
-            voffo[h] = row * (int)o_ld + chunk;
+    for (int h = 0; h < 2; ++h) {
+        const int row = 16 * (wave * 2 + h) + (lane >> 2);
+        const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
+        voff[h] = (wave * 2 + h) * (int)blk + lane * 16;
+        voffo[h] = row * (int)o_ld + chunk;
+    }
+    // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words
+    const bool sc_b = wave >= 4;
+    const int vsc = (64 * (wave & 3) + lane) * 4;
+    const uint8_t* const sc_tbl = sc_b ? Bs_rows : As;   // this wavefront's step-major scale array
+    const int64_t sc_total = sc_b ? N : T;               // its rows per step
+
+    // Step st of tile tl: FP4 codes + scales for st < nkb, the 64-byte column slice
+    // (st - nkb) of X_O / W_O for BF16 steps, and a null descriptor past the tile's
+    // steps or for no tile (zero range: the loads return zeros and touch no memory).
+    // Every step issues exactly DMA_PER_STAGE loads per wavefront, so the outstanding
+    // count, and with it every wait below, is the same on every step.
+    struct Src {
+        v4i a, b, sc;   // A and B operands, this wavefront's scale words
+        int so, fp4;
+    };
+    // Word-by-word scalar selects (a select of whole descriptors is lowered to a
+    // table in scratch memory).
+    auto pick = [&](bool c1, v4i x, bool c2, v4i y) __attribute__((always_inline)) {
+        v4i r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = __builtin_amdgcn_readfirstlane(c1 ? x[w] : (c2 ? y[w] : srd0[w]));
+        return r;
+    };
+    auto src_of = [&](const Tile& tl, int st) __attribute__((always_inline)) {
+        Src r;
+        const bool fp4 = tl.valid && st < nkb, bf = tl.valid && !fp4 && st < nsteps;
+        const int sts = fp4 ? st : 0;
+        const int64_t ra = rows_a_of(tl), rb = rows_b_of(tl);
+        r.fp4 = fp4;
+        r.a = pick(fp4, make_srd(Aq + (tl.t0 / 16) * blk, (uint32_t)((ra + 15) / 16 * blk)),
+                   bf, make_srd(XO + tl.t0 * k_ld, (uint32_t)(ra * o_ld)));
+        r.b = pick(fp4, make_srd(Bq + (tl.f0 / 16) * blk, (uint32_t)((rb + 15) / 16 * blk)),
+                   bf, make_srd(WO + tl.f0 * k_ld, (uint32_t)(rb * o_ld)));
+        r.sc = pick(fp4, make_srd(sc_tbl + ((int64_t)sts * sc_total + (sc_b ? tl.f0 : tl.t0)) * 4,
+                                  (uint32_t)((sc_b ? rb : ra) * 4)), false, srd0);
+        r.so = fp4 ? st * 1024 : (bf ? (st - nkb) * 64 : 0);
+        return r;
+    };
+    // The common case, an FP4 step of the current tile, with the per-tile parts
+    // precomputed: only the scale descriptor's base and the code offset move per step
+    // (rebuilding and selecting every descriptor each step would cost more scalar
+    // instructions than the scalar unit issues in a step's MFMA time).
+    struct Fast {
+        v4i a, b;
+        const uint8_t* sc;   // this wavefront's scale words of step 0
+        uint32_t sc_bytes;
+    };
+    auto fast_of = [&](const Tile& tl) __attribute__((always_inline)) {
+        Fast f;
+        const int64_t ra = rows_a_of(tl), rb = rows_b_of(tl);
+        f.a = make_srd(Aq + (tl.t0 / 16) * blk, (uint32_t)((ra + 15) / 16 * blk));
+        f.b = make_srd(Bq + (tl.f0 / 16) * blk, (uint32_t)((rb + 15) / 16 * blk));
+        f.sc = sc_tbl + (sc_b ? tl.f0 : tl.t0) * 4;
+        f.sc_bytes = (uint32_t)((sc_b ? rb : ra) * 4);
+        return f;
+    };
+    auto fast_src = [&](const Fast& f, int st) __attribute__((always_inline)) {
+        Src r;
+        r.fp4 = 1;
+        r.a = f.a;
+        r.b = f.b;
+        r.sc = make_srd(f.sc + (int64_t)st * sc_total * 4, f.sc_bytes);
+        r.so = st * 1024;
+        return r;
+    };
+    auto slot_of = [&](int g) __attribute__((always_inline)) {   // LDS address of ring slot g % STAGES
+        return lds0 + (uint32_t)((g & (STAGES - 1)) * SLOT_BYTES);
+    };
+    // live = false sends the (null) load to this wavefront's scratch KiB instead
+    const uint32_t spare = lds0 + STAGES * SLOT_BYTES + wave * 1024;
+    auto dma_code = [&](const Src& r, uint32_t slot, int h, int which, bool live = true) __attribute__((always_inline)) {
+        const int vo = r.fp4 ? voff[h] : voffo[h];
+        const uint32_t dst = slot + (which == 0 ? A_OFF : B_OFF) + (wave * 2 + h) * 1024;
+        dma16(which == 0 ? r.a : r.b, live ? dst : spare, vo, r.so);
+    };
+    auto dma_scale = [&](const Src& r, uint32_t slot, bool live = true) __attribute__((always_inline)) {
+        const uint32_t dst = slot + (sc_b ? BS_OFF : AS_OFF) + (wave & 3) * 256;
+        dma4(r.sc, live ? dst : spare, vsc, 0);
+    };
+    auto issue = [&](const Src& r, uint32_t slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 1);
+        dma_scale(r, slot);
+    };
+
+    // fragments of one half-step (64 FP4 codes or 16 bf16 values per row): 2 weight
+    // + 4 activation operands of 16 bytes, at chunk 2h + lane/32 of the 64-byte row
+    struct Frags {
+        v4i b[FF], a[FT];          // 16 bytes per operand (32 FP4 codes or 8 bf16)
+    };
+    struct Scales {
+        uint32_t b[FF], a[FT];     // raw scale words of a step; the lane's byte is selected at use
+    };
+    // g is the ring index of the step (its slot is g % STAGES)
+    auto load_b = [&](Frags& f, int g, int h, int i) __attribute__((always_inline)) {
+        const uint8_t* slot = smem + (g & (STAGES - 1)) * SLOT_BYTES;
+        const int r = wf * 64 + i * 32 + l32;
+        const uint4 q = *reinterpret_cast<const uint4*>(slot + B_OFF + swz(r, 2 * h + lh));
+        f.b[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+    };
+    auto load_a = [&](Frags& f, int g, int h, int j) __attribute__((always_inline)) {
+        const uint8_t* slot = smem + (g & (STAGES - 1)) * SLOT_BYTES;
+        const int r = wt * 128 + j * 32 + l32;
+        const uint4 q = *reinterpret_cast<const uint4*>(slot + A_OFF + swz(r, 2 * h + lh));
+        f.a[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+    };
+    auto load_scale = [&](Scales& c, int g, int o) __attribute__((always_inline)) {   // o-th of 6 words
+        const uint8_t* slot = smem + (g & (STAGES - 1)) * SLOT_BYTES;
+        if (o < FF) c.b[o] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[wf * 64 + o * 32 + l32];
+        else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * 128 + (o - FF) * 32 + l32];
+    };
+    auto load_half = [&](Frags& f, int g, int h, int o) __attribute__((always_inline)) {   // o-th of 6 operand reads
+        if (o < FF) load_b(f, g, h, o);
+        else load_a(f, g, h, o - FF);
+    };
+
+    v16f acc[FF][FT];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FF; ++i)
+#pragma unroll
+            for (int j = 0; j < FT; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    };
+    // one MFMA of a half-step; sh selects the lane's E8M0 byte of the scale words
+    auto mma_fp4 = [&](const Frags& f, const Scales& c, int h, int i, int j) __attribute__((always_inline)) {
+        const int sh = 8 * (2 * h + lh);
+        const v8i b = v8i{f.b[i][0], f.b[i][1], f.b[i][2], f.b[i][3], 0, 0, 0, 0};
+        const v8i a = v8i{f.a[j][0], f.a[j][1], f.a[j][2], f.a[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b, a, acc[i][j], 4, 4, 0, (int)(c.b[i] >> sh), 0, (int)(c.a[j] >> sh));
+    };
+    auto mma_bf16 = [&](const Frags& f, int i, int j) __attribute__((always_inline)) {
+        const v8bf wb = __builtin_bit_cast(v8bf, f.b[i]);
+        const v8bf xa = __builtin_bit_cast(v8bf, f.a[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, xa, acc[i][j], 0, 0, 0);
+    };
+
+    // Epilogue of tile tl.  Lane l holds token l32 and features 8q + 4*lh + r of each
+    // MFMA tile; the wavefront restages its 128 x 64 sub-tile 16 tokens at a time
+    // through its own part of a free ring slot, so that every store instruction writes
+    // 4 whole rows of 64 features (256 contiguous bytes each) instead of 32 rows x 32
+    // bytes.
+    constexpr int SROW = 64 + 4;   // staged row stride in floats (16 bytes of padding)
+    static_assert((G_THREADS / 64) * 16 * SROW * 4 <= SLOT_BYTES, "staging fits one ring slot");
+    auto epilogue = [&](const Tile& tl, int g) __attribute__((always_inline)) {
+        float* stage = reinterpret_cast<float*>(smem + (g & (STAGES - 1)) * SLOT_BYTES) + wave * (16 * SROW);
+        const bool full = rows_a_of(tl) == BT && rows_b_of(tl) == BF && vec_store;
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if ((l32 >> 4) == hh) {
+#pragma unroll
+                    for (int i = 0; i < FF; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<v4f*>(stage + (l32 & 15) * SROW + i * 32 + 8 * q + 4 * lh) =
+                                v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]};
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = (lane >> 4) + 4 * k;
+                    const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
+                    const int64_t t = tl.t0 + wt * 128 + j * 32 + hh * 16 + r;
+                    const int64_t n = tl.f0 + wf * 64 + (lane & 15) * 4;
+                    if constexpr (GELU) {
+                        const uint32_t h0 = gelu_tanh_bf16(v[0]), h1 = gelu_tanh_bf16(v[1]);
+                        const uint32_t h2 = gelu_tanh_bf16(v[2]), h3 = gelu_tanh_bf16(v[3]);
+                        if (full) {
+                            *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                        } else if (t < T) {
+                            if (vec_store && n + 3 < N) {
+                                *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                            } else {
+                                const uint32_t hv[4] = {h0, h1, h2, h3};
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (n + e < N) H[t * N + n + e] = (uint16_t)hv[e];
+                            }
+                        }
+                    } else {
+                        if (full) {
+                            *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                        } else if (t < T) {
+                            if (vec_store && n + 3 < N) {
+                                *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (n + e < N) Y[t * N + n + e] = v[e];
+                            }
+                        }
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next half overwrites it
+            }
         }
-        // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words
-        const bool sc_b = wave >= 4;
-        const int vsc = (64 * (wave & 3) + lane) * 4;
+    };
 
-        // Step st of the ring: FP4 codes + scales for st < nkb, the 64-byte column
-        // slice (st - nkb) of X_O / W_O for BF16 steps, and a null descriptor past the
-        // end (zero range: the loads return zeros and touch no memory).  Every step
-        // issues exactly DMA_PER_STAGE loads per wavefront, so the outstanding count,
-        // and with it every wait below, is the same on every iteration.
-        struct Src {
-            v4i a, b, as, bs;
-            int so, ss, fp4;
-        };
-        // Word-by-word scalar selects (a select of whole descriptors is lowered to a
-        // table in scratch memory).
-        auto pick = [&](bool c1, v4i x, bool c2, v4i y) __attribute__((always_inline)) {
-            v4i r;
+    // Pipeline.  MFMAs issue in order, so the LDS fragment reads and the DMA issue
+    // are interleaved one by one between the MFMAs of the other half-step, where
+    // they co-execute with the matrix pipe (sched_barrier pins the order):
+    //   half 0 of step st: 16 MFMAs on f0, interleaved with the 8 fragment reads of
+    //                      half 1 (f1);
+    //   sync:              wait for step st+1's DMA and for this wavefront's reads
+    //                      of slot st, then one barrier (slot st is free, slot st+1
+    //                      visible);
+    //   half 1 of step st: 16 MFMAs on f1, interleaved with the 8 reads of half 0
+    //                      of step st+1 (f0) and the 10 DMAs refilling slot st with
+    //                      step st+STAGES.
+    // At the sync point steps st+1..st+STAGES-1 are in flight; waiting for all but
+    // the last STAGES-2 of them (vmcnt 10) leaves step st+1 landed.  Loads complete in
+    // issue order among themselves, so a wait for at most n outstanding operations
+    // leaves every load landed that has at least n loads issued after it.  Across a
+    // tile boundary more is issued after the next tile's steps 1 and 2 (the null
+    // loads of the last step, the epilogue's stores, the deferred refill), which only
+    // makes those two waits stricter.  The FP4 steps run first, then the BF16 steps
+    // of the outlier branch on the same ring.
+    static_assert(STAGES == 4 && DMA_PER_STAGE == 5, "vmcnt immediates below assume 4 x 5");
+    Tile cur = tile_at(id);
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                r[w] = __builtin_amdgcn_readfirstlane(c1 ? x[w] : (c2 ? y[w] : srd0[w]));
-            return r;
-        };
-        auto src_of = [&](int st) __attribute__((always_inline)) {
-            Src r;
-            const bool fp4 = st < nkb, bf = !fp4 && st < nsteps;
-            r.fp4 = fp4;
-            r.a = pick(fp4, srdA, bf, srdXO);
-            r.b = pick(fp4, srdB, bf, srdWO);
-            r.as = pick(fp4, scale_srd(As, fp4 ? st : 0, T, t0, rows_a), false, srd0);
-            r.bs = pick(fp4, scale_srd(Bs_rows, fp4 ? st : 0, N, f0, rows_b), false, srd0);
-            r.so = fp4 ? st * 1024 : (bf ? (st - nkb) * 64 : 0);
-            r.ss = 0;
-            return r;
-        };
-        auto dma_code = [&](const Src& r, uint32_t slot, int h, int which) __attribute__((always_inline)) {
-            const int vo = r.fp4 ? voff[h] : voffo[h];
-            if (which == 0) dma16(r.a, slot + A_OFF + (wave * 2 + h) * 1024, vo, r.so);
-            else dma16(r.b, slot + B_OFF + (wave * 2 + h) * 1024, vo, r.so);
-        };
-        auto dma_scale = [&](const Src& r, uint32_t slot) __attribute__((always_inline)) {
-            dma4(sc_b ? r.bs : r.as, slot + (sc_b ? BS_OFF : AS_OFF) + (wave & 3) * 256, vsc, r.ss);
-        };
-        auto issue = [&](int st) __attribute__((always_inline)) {
-            const Src r = src_of(st);
-            const uint32_t slot = lds0 + (uint32_t)((st % STAGES) * SLOT_BYTES);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 0);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 1);
-            dma_scale(r, slot);
-        };
-
-        // fragments of one half-step (64 FP4 codes or 16 bf16 values per row): 4 weight
-        // + 4 activation operands of 16 bytes, at chunk 2h + lane/32 of the 64-byte row
-        struct Frags {
-            v4i b[FF], a[FT];          // 16 bytes per operand (32 FP4 codes or 8 bf16)
-        };
-        struct Scales {
-            uint32_t b[FF], a[FT];     // raw scale words of a step; the lane's byte is selected at use
-        };
-        auto load_b = [&](Frags& f, int st, int h, int i) __attribute__((always_inline)) {
-            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
-            const int r = wf * 64 + i * 32 + l32;
-            const uint4 q = *reinterpret_cast<const uint4*>(slot + B_OFF + swz(r, 2 * h + lh));
-            f.b[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-        };
-        auto load_a = [&](Frags& f, int st, int h, int j) __attribute__((always_inline)) {
-            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
-            const int r = wt * 128 + j * 32 + l32;
-            const uint4 q = *reinterpret_cast<const uint4*>(slot + A_OFF + swz(r, 2 * h + lh));
-            f.a[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-        };
-        auto load_scale = [&](Scales& c, int st, int o) __attribute__((always_inline)) {   // o-th of 6 words
-            const uint8_t* slot = smem + (st % STAGES) * SLOT_BYTES;
-            if (o < FF) c.b[o] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[wf * 64 + o * 32 + l32];
-            else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * 128 + (o - FF) * 32 + l32];
-        };
-        auto load_half = [&](Frags& f, int st, int h, int o) __attribute__((always_inline)) {   // o-th of 6 operand reads
-            if (o < FF) load_b(f, st, h, o);
-            else load_a(f, st, h, o - FF);
-        };
-        // one MFMA of a half-step; sh selects the lane's E8M0 byte of the scale words
-        auto mma_fp4 = [&](const Frags& f, const Scales& c, int h, int i, int j) __attribute__((always_inline)) {
-            const int sh = 8 * (2 * h + lh);
-            const v8i b = v8i{f.b[i][0], f.b[i][1], f.b[i][2], f.b[i][3], 0, 0, 0, 0};
-            const v8i a = v8i{f.a[j][0], f.a[j][1], f.a[j][2], f.a[j][3], 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                b, a, acc[i][j], 4, 4, 0, (int)(c.b[i] >> sh), 0, (int)(c.a[j] >> sh));
-        };
-        auto mma_bf16 = [&](const Frags& f, int i, int j) __attribute__((always_inline)) {
-            const v8bf wb = __builtin_bit_cast(v8bf, f.b[i]);
-            const v8bf xa = __builtin_bit_cast(v8bf, f.a[j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, xa, acc[i][j], 0, 0, 0);
-        };
-
-        // Pipeline.  MFMAs issue in order, so the LDS fragment reads and the DMA issue
-        // are interleaved one by one between the MFMAs of the other half-step, where
-        // they co-execute with the matrix pipe (sched_barrier pins the order):
-        //   half 0 of step st: 16 MFMAs on f0, interleaved with the 8 fragment reads of
-        //                      half 1 (f1);
-        //   sync:              wait for step st+1's DMA and for this wavefront's reads
-        //                      of slot st, then one barrier (slot st is free, slot st+1
-        //                      visible);
-        //   half 1 of step st: 16 MFMAs on f1, interleaved with the 8 reads of half 0
-        //                      of step st+1 (f0) and the 10 DMAs refilling slot st with
-        //                      step st+STAGES.
-        // At the sync point steps st+1..st+STAGES-1 are in flight; waiting for all but
-        // the last STAGES-2 of them (vmcnt 20) leaves step st+1 landed.  The FP4 steps
-        // run first, then the BF16 steps of the outlier branch on the same ring.
-        static_assert(STAGES == 4 && DMA_PER_STAGE == 5, "vmcnt immediates below assume 4 x 5");
-#pragma unroll
-        for (int st = 0; st < STAGES; ++st) issue(st);
-        asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-        __syncthreads();
-        Frags f0, f1;
-        Scales c0, c1;                 // scale words of the current and of the next step
+    for (int st = 0; st < STAGES; ++st) issue(src_of(cur, st), slot_of(st));
+    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    __syncthreads();
+    Frags f0, f1;
+    Scales c0, c1;                 // scale words of the current and of the next step
+    // half 0 fragments and scale words of a tile's first step (ring index g)
+    auto load_first = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
         for (int o = 0; o < FF + FT; ++o) {
-            load_half(f0, 0, 0, o);
-            load_scale(c0, 0, o);
+            load_half(f0, g, 0, o);
+            load_scale(c0, g, o);
         }
+    };
+    load_first(0);
+    zero_acc();
 
-        constexpr int NM = FF * FT;   // MFMAs per half-step
-        auto sync_and_refill_setup = [&](int st) __attribute__((always_inline)) {
+    constexpr int NM = FF * FT;   // MFMAs per half-step
+    int base = 0;                 // ring index of the current tile's step 0
+    for (;;) {
+        const int64_t next_id = id + gridDim.x;
+        const Tile nxt = tile_at(next_id);
+        const Fast fc = fast_of(cur);
+        auto sync = [&]() __attribute__((always_inline)) {
             asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot st fully read
             __syncthreads();
         };
-        auto half1 = [&](int st, bool fp4) __attribute__((always_inline)) {
-            const Src r = src_of(st + STAGES);
-            const uint32_t slot = lds0 + (uint32_t)(((st + STAGES) % STAGES) * SLOT_BYTES);
+        // half 1 of step st; its DMA fetches ring step st + STAGES: this tile's, the
+        // next tile's first steps, or at the last step nothing: null loads into the
+        // spare KiB keep the load count of every step the same, and the refill of this
+        // slot waits until the epilogue has staged through it
+        auto refill = [&](int st) __attribute__((always_inline)) {
+            const int s4 = st + STAGES;
+            const bool here = s4 < ns;
+            Tile tl = here ? cur : nxt;
+            tl.valid = tl.valid && st + 1 < ns;
+            return src_of(tl, here ? s4 : s4 - ns);
+        };
+        auto half1 = [&](int st, bool fp4, const Scales& cs, Scales& nx, const Src& r, bool dma)
+            __attribute__((always_inline)) {
+            const uint32_t slot = slot_of(base + st);
 #pragma unroll
             for (int s = 0; s < NM; ++s) {
-                if (fp4) mma_fp4(f1, c0, 1, s % FF, s / FF);
+                if (fp4) mma_fp4(f1, cs, 1, s % FF, s / FF);
                 else mma_bf16(f1, s % FF, s / FF);
                 if (s < FF + FT) {
-                    load_half(f0, st + 1, 0, s);
-                    load_scale(c1, st + 1, s);
+                    load_half(f0, base + st + 1, 0, s);
+                    load_scale(nx, base + st + 1, s);
                 }
-                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0);
-                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1);
-                if (s == 5) dma_scale(r, slot);
+                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0, dma);
+                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1, dma);
+                if (s == 5) dma_scale(r, slot, dma);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
         // FP4 steps, unrolled by two so that the scale words of the current and the
         // next step alternate between c0 and c1 without a copy (a copy would wait for
         // every outstanding LDS read at the end of each step)
-        auto fp4_step = [&](int st, Scales& cur, Scales& nxt) __attribute__((always_inline)) {
+        auto fp4_step = [&](int st, const Scales& cs, Scales& nx, bool fast) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NM; ++s) {
-                mma_fp4(f0, cur, 0, s % FF, s / FF);
-                if (s < FF + FT) load_half(f1, st, 1, s);
+                mma_fp4(f0, cs, 0, s % FF, s / FF);
+                if (s < FF + FT) load_half(f1, base + st, 1, s);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            sync_and_refill_setup(st);
+            sync();
             __builtin_amdgcn_sched_barrier(0);
-            const Src r = src_of(st + STAGES);
-            const uint32_t slot = lds0 + (uint32_t)(((st + STAGES) % STAGES) * SLOT_BYTES);
-#pragma unroll
-            for (int s = 0; s < NM; ++s) {
-                mma_fp4(f1, cur, 1, s % FF, s / FF);
-                if (s < FF + FT) {
-                    load_half(f0, st + 1, 0, s);
-                    load_scale(nxt, st + 1, s);
-                }
-                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0);
-                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1);
-                if (s == 5) dma_scale(r, slot);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            if (fast) half1(st, true, cs, nx, fast_src(fc, st + STAGES), true);
+            else half1(st, true, cs, nx, refill(st), st + 1 < ns);
         };
-        int st = 0;
-        for (; st + 1 < nkb; st += 2) {
-            fp4_step(st, c0, c1);
-            fp4_step(st + 1, c1, c0);
-        }
-        if (st < nkb) fp4_step(st, c0, c1);
-        for (st = nkb; st < nsteps; ++st) {
+        // BF16 steps (and the null steps that pad short K); the scale words they load
+        // are unused here
+        auto bf16_step = [&](int st) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NM; ++s) {
                 mma_bf16(f0, s % FF, s / FF);
-                if (s < FF + FT) load_half(f1, st, 1, s);
+                if (s < FF + FT) load_half(f1, base + st, 1, s);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            sync_and_refill_setup(st);
+            sync();
             __builtin_amdgcn_sched_barrier(0);
-            half1(st, false);
+            half1(st, false, c1, c0, refill(st), st + 1 < ns);
+        };
+        int st = 0;
+        // steps whose refill is this tile's FP4 step st + STAGES
+        for (; st + 1 + STAGES < nkb; st += 2) {
+            fp4_step(st, c0, c1, true);
+            fp4_step(st + 1, c1, c0, true);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+        for (; st + 1 < nkb; st += 2) {
+            fp4_step(st, c0, c1, false);
+            fp4_step(st + 1, c1, c0, false);
+        }
+        if (st < nkb) fp4_step(st++, c0, c1, false);
+        for (; st < ns; ++st) bf16_step(st);
 
-    // ---- epilogue.  Lane l holds token l32 and features 8q + 4*lh + r of each MFMA
-    // tile; the wavefront restages each 32-token slab of its 128 x 64 sub-tile through
-    // LDS (the ring is idle now) so that every store instruction writes 4 whole rows
-    // of 64 features (256 contiguous bytes each) instead of 32 rows x 32 bytes.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    {
-        constexpr int SROW = 64 + 4;   // staged row stride in floats (16 bytes of padding)
-        static_assert((G_THREADS / 64) * 32 * SROW * 4 <= STAGES * SLOT_BYTES, "staging fits the ring");
-        float* stage = reinterpret_cast<float*>(smem) + wave * (32 * SROW);
-        const bool full = (T - t0 >= BT) && (N - f0 >= BF) && vec_store;
-#pragma unroll
-        for (int j = 0; j < FT; ++j) {
-#pragma unroll
-            for (int i = 0; i < FF; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<v4f*>(stage + l32 * SROW + i * 32 + 8 * q + 4 * lh) =
-                        v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r = (lane >> 4) + 4 * k;
-                const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
-                const int64_t t = t0 + wt * 128 + j * 32 + r;
-                const int64_t n = f0 + wf * 64 + (lane & 15) * 4;
-                if constexpr (GELU) {
-                    const uint32_t h0 = gelu_tanh_bf16(v[0]), h1 = gelu_tanh_bf16(v[1]);
-                    const uint32_t h2 = gelu_tanh_bf16(v[2]), h3 = gelu_tanh_bf16(v[3]);
-                    if (full) {
-                        *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                    } else if (t < T) {
-                        if (vec_store && n + 3 < N) {
-                            *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                        } else {
-                            const uint32_t hv[4] = {h0, h1, h2, h3};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (n + e < N) H[t * N + n + e] = (uint16_t)hv[e];
-                        }
-                    }
-                } else {
-                    if (full) {
-                        *reinterpret_cast<v4f*>(Y + t * N + n) = v;
-                    } else if (t < T) {
-                        if (vec_store && n + 3 < N) {
-                            *reinterpret_cast<v4f*>(Y + t * N + n) = v;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (n + e < N) Y[t * N + n + e] = v[e];
-                        }
-                    }
-                }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slab read before the next overwrites it
-        }
+        // The last step's half 1 has already read the next tile's first fragments; they
+        // are read again below so that no register holds them across the epilogue.
+        epilogue(cur, base + ns - 1);
+        if (!nxt.valid) break;
+        __syncthreads();   // every wavefront is done with the staging slot
+        issue(src_of(nxt, STAGES - 1), slot_of(base + ns - 1));
+        base += ns;
+        cur = nxt;
+        id = next_id;
+        load_first(base);
+        zero_acc();
     }
+}
+
+// One persistent workgroup per CU (the LDS ring admits one), at most one per tile.
+static int64_t gemm_grid(int64_t tiles) {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev] = c;
+    }
+    return tiles < cus[dev] ? tiles : cus[dev];
 }
 
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
@@ -465,11 +572,12 @@ hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
     if ((int64_t)BT * (d.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     // vector stores: 16 bytes (fp32) or 8 bytes (bf16) per lane, aligned when every row is
     const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)out & 15u) == 0);
+    const unsigned grid = (unsigned)gemm_grid(tiles);
     if (gelu_bf16)
-        gemm_w4a4_kernel<true><<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
+        gemm_w4a4_kernel<true><<<dim3(grid), G_THREADS, 0, st>>>(
             Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
     else
-        gemm_w4a4_kernel<false><<<dim3((unsigned)tiles), G_THREADS, 0, st>>>(
+        gemm_w4a4_kernel<false><<<dim3(grid), G_THREADS, 0, st>>>(
             Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
     return hipGetLastError();
 }
