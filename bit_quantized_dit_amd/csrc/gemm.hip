@@ -70,7 +70,7 @@ constexpr int BS_OFF = AS_OFF + BT * 4;
 constexpr int SLOT_BYTES = BS_OFF + BF * 4;  // 34 KiB
 constexpr int STAGES = 4;
 constexpr int DMA_PER_STAGE = 5;             // per wavefront: 2 A + 2 B 1-KiB code blocks, 1 scale block
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 
 // Raw buffer descriptor (gfx9 family): base, 16 high address bits, no stride,
