@@ -49,7 +49,7 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 }
 
 // Eight E2M1 nibbles (element 2i in the low nibble of byte i) for finite values whose
-// group scale code is `code` (< 0xFF).  The conversion divides by the fp32 scale 2^E
+// group scale code is `code` (< 0xFF; for 0xFF the result is meaningless).  The conversion divides by the fp32 scale 2^E
 // and rounds to nearest even, saturating at 6; E = -127 is the subnormal 2^-127.
 __device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
     const float scale = __uint_as_float(code == 0u ? 0x00400000u : code << 23);
@@ -67,13 +67,24 @@ __device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
 // as_t points at this token's scale slot of step 0 in the step-major A_s
 // ([k_pad/128][T][4]); step kb's slot is as_t + kb * as_step.  k_pad is a multiple of
 // 128, so the four lanes of a quad are active together.
+// A pass of the NT lanes spans NT / 16 whole 128-code steps, so a lane's byte
+// position within a step is the same on every pass and only the step advances: the
+// A_q offset (32-bit, from the token's uniform block base), the A_s pointer and the
+// LDS position all move by constants.  k_pad < 2^31 (the host checks it).
 template <int NT>
 __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, uint8_t* Aq, int64_t t,
                                              uint8_t* as_t, int64_t as_step) {
+    static_assert(NT % 16 == 0, "whole steps per pass");
     const int r = (int)(t & 15);
-    uint8_t* aq_blk = Aq + (((t >> 4) * (k_pad / 128)) << 10) + (r << 6);
-    for (int64_t p0 = (int64_t)threadIdx.x * 8; p0 < k_pad; p0 += NT * 8) {
-        const float* src = row + lds_pos(p0);
+    uint8_t* const aq_blk = Aq + (((t >> 4) * (k_pad / 128)) << 10) + (r << 6);
+    const int kp = (int)k_pad;
+    const int first = (int)threadIdx.x * 8;
+    uint32_t aq_off = ((uint32_t)(first >> 7) << 10) |
+                      (((((uint32_t)first >> 5) & 3u) ^ (uint32_t)(r >> 2)) << 4) | (((uint32_t)first & 31u) >> 1);
+    uint8_t* as_p = as_t + (int64_t)(first >> 7) * as_step + ((first >> 5) & 3);
+    int lp = (int)lds_pos(first);
+    for (int p0 = first; p0 < kp; p0 += NT * 8, aq_off += (NT / 16) << 10, as_p += (NT / 16) * as_step, lp += 9 * NT) {
+        const float* src = row + lp;
         const float4 a = *reinterpret_cast<const float4*>(src);
         const float4 b = *reinterpret_cast<const float4*>(src + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -84,10 +95,11 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
             m = q > m ? q : m;
         }
         const uint32_t code = e8m0_from_absbits(quad_max_u32(m));
-        const uint32_t word = code == 0xFFu ? 0u : e2m1_word8(v, code);
-        const int byte = (int)(p0 % 128) / 2;   // within the 64-byte row slice of the step
-        *reinterpret_cast<uint32_t*>(aq_blk + ((p0 / 128) << 10) + ((((byte >> 4) ^ (r >> 2)) << 4) | (byte & 15))) = word;
-        if ((threadIdx.x & 3) == 0) as_t[(p0 / 128) * as_step + (p0 / 32) % 4] = (uint8_t)code;
+        // converted unconditionally (a NaN/Inf block's scale 2^128 gives some nibbles)
+        // and then replaced by zero nibbles, without a branch
+        const uint32_t word = e2m1_word8(v, code);
+        *reinterpret_cast<uint32_t*>(aq_blk + aq_off) = code == 0xFFu ? 0u : word;
+        if ((threadIdx.x & 3) == 0) *as_p = (uint8_t)code;
     }
 }
 
@@ -190,7 +202,9 @@ constexpr int ap_depth() {
     return regs * 4 <= 10 ? 4 : regs * 3 <= 10 ? 3 : regs * 2 <= 10 ? 2 : 1;
 }
 
-// Fast path: d_in even, d_in <= 2 * NT * MAXM.  Lane i owns the column pairs
+// Fast path: d_in even, 2 * NT * (MAXM - 1) < d_in <= 2 * NT * MAXM (the launcher
+// takes the smallest MAXM that fits), so every pass but the last covers all NT
+// lanes.  Lane i owns the column pairs
 // 2(i + NT*m), 2(i + NT*m) + 1: one 4-byte (bf16) or 8-byte (fp32) load per pair, so
 // a wavefront's loads of one m are one contiguous run.  Rows are read through a
 // buffer descriptor per row (range d_in elements; zero range past the workgroup's
@@ -252,7 +266,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
             for (int m = 0; m < MAXM; ++m) {
                 const float lo = Pair<XT>::lo(xv[d][m]), hi = Pair<XT>::hi(xv[d][m]);
                 const float qlo = div_by_s(lo, rv[m][0]), qhi = div_by_s(hi, rv[m][1]);
-                if ((int64_t)threadIdx.x + (int64_t)NT * m < npairs) {
+                if (m + 1 < MAXM || (int64_t)threadIdx.x + (int64_t)NT * m < npairs) {
                     row[slot[m][0]] = outl[m][0] ? lo : qlo;
                     row[slot[m][1]] = outl[m][1] ? hi : qhi;
                 }
@@ -310,6 +324,7 @@ static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uin
     W4A4_AP_PAIRS(512, 4)
     W4A4_AP_PAIRS(512, 5)
     W4A4_AP_PAIRS(512, 6)
+    W4A4_AP_PAIRS(512, 7)
     W4A4_AP_PAIRS(512, 8)
     W4A4_AP_PAIRS(1024, 5)
     W4A4_AP_PAIRS(1024, 6)

@@ -51,7 +51,6 @@
 
 namespace w4a4 {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -72,43 +71,6 @@ constexpr int STAGES = 4;
 constexpr int DMA_PER_STAGE = 5;             // per wavefront: 2 A + 2 B 1-KiB code blocks, 1 scale block
 constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
-
-// Raw buffer descriptor (gfx9 family): base, 16 high address bits, no stride,
-// num_records = byte range, word 3 = 32-bit data format.  Out-of-range loads read 0.
-__device__ __forceinline__ v4i make_srd(const void* p, uint32_t nbytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// Global -> LDS without VGPRs: lane i's 16 (4) bytes land at LDS m0 + 16*i (4*i).
-// The compiler does not track these writes, so the kernel waits on vmcnt itself
-// before the barrier that publishes a slot.  The instruction has no register
-// results; its address operands are read at issue.  Descriptor, LDS base and
-// soffset are wave-uniform by construction; readfirstlane only tells the compiler.  One wait state separates the
-// SALU write of m0 from the DMA that reads it.
-__device__ __forceinline__ v4i uniform(v4i r) {
-    return v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
-               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
-}
-__device__ __forceinline__ void dma16(v4i srd, uint32_t lds, int voff, int soff) {
-    srd = uniform(srd);
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    soff = __builtin_amdgcn_readfirstlane(soff);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(srd), "s"(soff));
-}
-__device__ __forceinline__ void dma4(v4i srd, uint32_t lds, int voff, int soff) {
-    srd = uniform(srd);
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    soff = __builtin_amdgcn_readfirstlane(soff);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(srd), "s"(soff));
-}
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return row * ROW_BYTES + ((chunk ^ ((row >> 2) & 3)) << 4);
