@@ -52,7 +52,10 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 // group scale code is `code` (< 0xFF; for 0xFF the result is meaningless).  The conversion divides by the fp32 scale 2^E
 // and rounds to nearest even, saturating at 6; E = -127 is the subnormal 2^-127.
 __device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
-    const float scale = __uint_as_float(code == 0u ? 0x00400000u : code << 23);
+    // 2^E, E = code - 127: the biased exponent field, or the subnormal 2^-127 for code 0
+    // (code << 23 is at least 2^-126 otherwise, so a maximum selects)
+    const uint32_t sb = code << 23;
+    const float scale = __uint_as_float(sb > 0x00400000u ? sb : 0x00400000u);
     uint32_t w = 0;
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
@@ -99,7 +102,7 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
         // and then replaced by zero nibbles, without a branch
         const uint32_t word = e2m1_word8(v, code);
         *reinterpret_cast<uint32_t*>(aq_blk + aq_off) = code == 0xFFu ? 0u : word;
-        if ((threadIdx.x & 3) == 0) *as_p = (uint8_t)code;
+        *as_p = (uint8_t)code;   // the four lanes of the block store the same byte
     }
 }
 

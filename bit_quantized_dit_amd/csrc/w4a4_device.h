@@ -25,7 +25,8 @@ __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x
 // E8M0 code from the bit pattern of the group's largest |x|.
 __device__ __forceinline__ uint32_t e8m0_from_absbits(uint32_t amax_bits) {
     const uint32_t e = amax_bits >> 23;
-    return e == 0xFFu ? 0xFFu : (e > 2u ? e - 2u : 0u);
+    const uint32_t c = __builtin_elementwise_sub_sat(e, 2u);   // max(e - 2, 0)
+    return e == 0xFFu ? 0xFFu : c;
 }
 
 // 2^-E as a binary32 for a finite scale code c (c <= 252 for finite amax, so the
