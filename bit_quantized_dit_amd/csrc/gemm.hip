@@ -77,18 +77,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // Block id -> (token tile, feature tile): XCD-contiguous ranges, grouped order.
-__device__ __forceinline__ void tile_of(int64_t bid, int64_t nt_m, int64_t nt_n, int64_t& tm, int64_t& tn) {
-    const int64_t total = nt_m * nt_n;
-    const int64_t q = total / NUM_XCD, r = total % NUM_XCD;
-    const int64_t x = bid % NUM_XCD, j = bid / NUM_XCD;
-    const int64_t id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
-    const int64_t per_group = GROUP_M * nt_n;
-    const int64_t g = id / per_group;
-    const int64_t first_m = g * GROUP_M;
-    const int64_t gsize = nt_m - first_m < GROUP_M ? nt_m - first_m : GROUP_M;
-    const int64_t in_g = id % per_group;
-    tm = first_m + in_g % gsize;
+// 32-bit arithmetic: the launcher keeps the tile count below 2^31.
+__device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nt_m, uint32_t nt_n, uint32_t& tm, uint32_t& tn) {
+    const uint32_t total = nt_m * nt_n;
+    const uint32_t q = total / NUM_XCD, r = total % NUM_XCD;
+    const uint32_t x = bid % NUM_XCD, j = bid / NUM_XCD;
+    const uint32_t id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const uint32_t per_group = GROUP_M * nt_n;
+    const uint32_t g = id / per_group;
+    const uint32_t first_m = g * GROUP_M;
+    const uint32_t gsize = nt_m - first_m < (uint32_t)GROUP_M ? nt_m - first_m : (uint32_t)GROUP_M;
+    const uint32_t in_g = id - g * per_group;
     tn = in_g / gsize;
+    tm = first_m + (in_g - tn * gsize);
 }
 
 // GELU = false: out is fp32 Y [T][N].  GELU = true: out is bf16 H [T][N] with
@@ -141,10 +142,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     auto tile_at = [&](int64_t i) __attribute__((always_inline)) {
         Tile t;
         t.valid = i < ntiles;
-        int64_t tm = 0, tn = 0;
-        if (t.valid) tile_of(i, nt_m, nt_n, tm, tn);
-        t.t0 = tm * BT;
-        t.f0 = tn * BF;
+        uint32_t tm = 0, tn = 0;
+        if (t.valid) tile_of((uint32_t)i, (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
+        t.t0 = (int64_t)tm * BT;
+        t.f0 = (int64_t)tn * BF;
         return t;
     };
     auto rows_a_of = [&](const Tile& t) __attribute__((always_inline)) { return T - t.t0 < BT ? T - t.t0 : (int64_t)BT; };
