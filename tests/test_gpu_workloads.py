@@ -148,12 +148,16 @@ def test_workload5_ffn_block(orc, mini):
     _banner(f"  down: {st}")
 
 
-@pytest.mark.parametrize("T,d_in,d_out,k,layout", [(2600, 640, 7001, 24, 0), (2600, 640, 6912, 24, 1)])
+@pytest.mark.parametrize("T,d_in,d_out,k,layout", [(2600, 640, 7001, 24, 0), (2600, 640, 6912, 24, 1),
+                                                    (600, 100, 40000, 4, 0), (600, 60, 39999, 0, 0)])
 def test_many_tiles_per_workgroup_with_ragged_edges(orc, T, d_in, d_out, k, layout):
     """More output tiles than the persistent grid has workgroups, so workgroups run
     several tiles in a row, full and ragged ones (token tail, feature tail, and an
     output width that is not a multiple of 4): every output row and column at a tile
-    edge is checked, plus random samples."""
+    edge is checked, plus random samples.  The last two cases have fewer K steps than
+    the ring has slots (one FP4 step and one or no BF16 step), so the ring pads each
+    tile with null steps and the prefetch of the next tile starts within the current
+    tile's first steps."""
     spec = synth.WORKLOADS[2]
     _banner(f"many tiles T={T} d_in={d_in} d_out={d_out} k={k} layout={layout}")
     inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=256)
