@@ -24,18 +24,19 @@
 //
 // Tiling: a 512-thread workgroup (8 wavefronts, 2 token halves x 4 feature quarters,
 // two per SIMD) owns a 256-token x 256-feature output tile; each wavefront a
-// 128 x 64 sub-tile (4 x 2 MFMA tiles, 128 fp32 accumulators per lane in AGPRs), so
+// 128 x 64 sub-tile (4 x 2 MFMA tiles, 128 fp32 accumulator registers per lane), so
 // that one wavefront's LDS waits and barrier waits are covered by the MFMAs of its
-// SIMD partner.  The 256 x 256 tile keeps the global traffic per
-// MFMA at the level that the per-CU vector memory path sustains.  The K loop walks 128-code steps
-// (64 bytes per row).  Operands move HBM/L2 -> LDS with buffer_load ... lds (no
-// VGPR staging) into a ring of STAGES slots; STAGES-1 steps are in flight while the
-// MFMAs of the current step run.  Each slot holds 256 + 256 rows of 64 bytes plus one
-// 32-bit word of four E8M0 codes per row (read from the step-major scale arrays, so
-// that one wavefront's 64 words are one contiguous 256-byte request).  After the FP4 steps the same ring streams
-// the outlier branch: 32 bf16 values of X_O and W_O per row are again 64 bytes, so
-// each BF16 step has the slot layout of an FP4 step (without scales) and feeds
-// v_mfma_f32_32x32x16_bf16 into the same accumulators.
+// SIMD partner.  The 256 x 256 tile (the largest whose fp32 accumulators fit the
+// CU's registers) keeps the global traffic per MFMA at the level that the per-CU
+// vector memory path sustains.  The K loop walks 128-code steps (64 bytes per row).
+// Operands move HBM/L2 -> LDS with buffer_load ... lds (no VGPR staging) into a ring
+// of STAGES slots; STAGES-1 steps are in flight while the MFMAs of the current step
+// run.  Each slot holds 256 + 256 rows of 64 bytes plus one 32-bit word of four E8M0
+// codes per row (read from the step-major scale arrays, so that one wavefront's 64
+// words are one contiguous 256-byte request).  After the FP4 steps the same ring
+// streams the outlier branch: 32 bf16 values of X_O and W_O per row are again 64
+// bytes, so each BF16 step has the slot layout of an FP4 step (without scales) and
+// feeds v_mfma_f32_32x32x16_bf16 into the same accumulators.
 // 16-byte chunks are XOR-swizzled by row so that fragment reads are bank-conflict
 // free (the DMA writes each wavefront's 1 KiB contiguously, so the swizzle lives in
 // the tiled code layout, and in the source addresses of the bf16 gather).
@@ -43,9 +44,11 @@
 // feature tail read as zero, with no masking in the loop.
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with its
-// own L2.  The linear block id is remapped so that each XCD owns a contiguous range
-// of tiles, and tiles are ordered in groups of GROUP_M token panels so that the
-// workgroups resident on one XCD share A (token) and B (feature) panels in its L2.
+// own L2, and the persistent workgroup b runs tiles b, b + G, b + 2G, ... with G a
+// multiple of 8, so all of its tiles map to one XCD.  The linear tile id is remapped
+// so that each XCD owns a contiguous range of tiles, ordered in groups of GROUP_M
+// token panels, so that the workgroups resident on one XCD share A (token) and B
+// (feature) panels in its L2.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
 
@@ -513,7 +516,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     }
 }
 
-// One persistent workgroup per CU (the LDS ring admits one), at most one per tile.
+// One persistent workgroup per CU (the LDS ring admits one), at most one per tile,
+// and a multiple of the XCD count, so that a workgroup's tiles stay on its XCD.
 static int64_t gemm_grid(int64_t tiles) {
     static int cus[64] = {0};
     int dev = 0;
@@ -523,7 +527,8 @@ static int64_t gemm_grid(int64_t tiles) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
         cus[dev] = c;
     }
-    return tiles < cus[dev] ? tiles : cus[dev];
+    const int64_t g = cus[dev] >= NUM_XCD ? cus[dev] / NUM_XCD * NUM_XCD : cus[dev];
+    return tiles < g ? tiles : g;
 }
 
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
