@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA (published)
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 LAYOUT_NAMES = {0: "1x32", 1: "32x32_tile", 2: "128x1_stripe"}
 
@@ -51,6 +52,27 @@ def measured_traffic(kernel: str, workload: str):
     if kernel == "gemm_w4a4" and m_src.group(1) != gemm_source_digest():
         return None
     return float(m_bytes.group(1))
+
+
+def copy_ceiling_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Device-to-device copy rate (read + write bytes per second, best of `reps`): the
+    practical HBM ceiling that act-prep's streaming is compared with."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return 2.0 * nbytes / best / 1e9
 
 
 def cpu_baseline(inp, s, O, layout, budget_s: float = 12.0):
@@ -260,18 +282,26 @@ def main():
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ap_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    gm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ap_all = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    gm_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ap_ms = float(np.mean(ap_all))
+    gm_ms = float(np.mean(gm_all))
     ms_step = wall * 1e3 / K
 
     flops = 2.0 * T * d_out * d_in
     k_j = d_in - k
     k_pad = packed.k_pad
-    ap_bytes = T * d_in * 2 + T * (k_pad // 2 + k_pad // 32 + k * 2)
+    x_bytes = 2 if spec.x_dtype == "bf16" else 4
+    ap_bytes = T * d_in * x_bytes + T * (k_pad // 2 + k_pad // 32 + k * 2)
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
-    log(f"[bench] act-prep {ap_ms * 1e3:.1f} us ({ap_bytes / (ap_ms * 1e-3) / 1e9:.0f} GB/s algorithmic), "
-        f"gemm {gm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s, "
-        f"{100 * gemm_tflops / PEAK_FP4_TFLOPS:.1f}% of MXFP4 peak), step {ms_step:.3f} ms")
+    # mixed roofline: the J branch at the MXFP4 peak plus the O branch at the BF16 peak
+    ideal_s = 2.0 * T * d_out * k_j / (PEAK_FP4_TFLOPS * 1e12) + 2.0 * T * d_out * k / (PEAK_BF16_TFLOPS * 1e12)
+    copy_gbs = copy_ceiling_gbs()
+    ap_gbs = ap_bytes / (ap_ms * 1e-3) / 1e9
+    log(f"[bench] act-prep {ap_ms * 1e3:.1f} us ({ap_gbs:.0f} GB/s algorithmic, {100 * ap_gbs / copy_gbs:.0f}% of the "
+        f"{copy_gbs:.0f} GB/s copy ceiling), gemm {gm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s, "
+        f"{100 * gemm_tflops / PEAK_FP4_TFLOPS:.1f}% of MXFP4 peak, {100 * ideal_s / (gm_ms * 1e-3):.1f}% of the "
+        f"mixed FP4/BF16 roofline), step {ms_step:.3f} ms")
     workload = spec.name
     traffic = measured_traffic("gemm_w4a4", workload)
 
@@ -295,6 +325,14 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_w4a4_kernel", "achieved": gemm_tflops,
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_FP4_TFLOPS,
                      "traffic": traffic},
+        "gemm": {"us_mean": gm_ms * 1e3, "us_median": float(np.median(gm_all)) * 1e3,
+                 "us_min": float(np.min(gm_all)) * 1e3,
+                 "mixed_roofline_frac": ideal_s / (gm_ms * 1e-3),
+                 "mixed_roofline_note": "(2 T d_out K_J / MXFP4 peak + 2 T d_out k / BF16 peak) / time"},
+        "act_prep": {"bound": "hbm", "us_mean": ap_ms * 1e3, "us_min": float(np.min(ap_all)) * 1e3,
+                     "algorithmic_bytes": ap_bytes, "achieved_gbs": ap_gbs,
+                     "frac_of_hbm_peak": ap_gbs / PEAK_HBM_GBS, "copy_ceiling_gbs": copy_gbs,
+                     "frac_of_copy_ceiling": ap_gbs / copy_gbs},
     }
     if not args.no_quality:
         log("[bench] quantization error report (ungated) ...")
