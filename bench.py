@@ -138,6 +138,24 @@ def quality(inp, X, W, spec, s, O, act_scale, tokens: int = 512):
     return out
 
 
+def search_report(Xc, W, layout, alphas=(0.5, 0.6, 0.7), ks=(0, 64, 128, 256)):
+    """The layer-wise alpha / k search on the calibration tokens (ungated): every
+    candidate's relative Frobenius output error against the unquantized product, the
+    choice, and the search's wall time (calibration, pack and the layer per candidate,
+    all in the library)."""
+    import torch
+
+    from bit_quantized_dit_amd import w4a4 as B
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    err, (a, b) = B.w4a4_search_alpha_k(Xc, W, list(alphas), list(ks), layout)
+    ms = (time.perf_counter() - t0) * 1e3
+    return {"calibration_tokens": int(Xc.shape[0]), "alphas": list(alphas), "ks": list(ks),
+            "errors": err.tolist(), "best": {"alpha": alphas[a], "k": ks[b]}, "ms": ms,
+            "criterion": "relative Frobenius error of Y on the calibration tokens vs X_cal W^T (fp32)"}
+
+
 def ffn_block(args):
     """The full FFN block at 57600 tokens: the up projection 5120 -> 13824 (32x32-tile
     weight scales) with GELU-tanh fused into its epilogue (bf16 H), then the down
@@ -338,6 +356,9 @@ def main():
         log("[bench] quantization error report (ungated) ...")
         result["quality"] = quality(inp, X, W, spec, s, O, act_scale)
         log(f"[bench] quality {result['quality']}")
+        log("[bench] layer-wise alpha / k search on the calibration tokens (ungated) ...")
+        result["search"] = search_report(Xc, W, spec.layout)
+        log(f"[bench] search best {result['search']['best']} in {result['search']['ms']:.0f} ms")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(inp, s, O, spec.layout)

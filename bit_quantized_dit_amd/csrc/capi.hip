@@ -81,14 +81,85 @@ int check_desc(const w4a4_packed* d) {
     return W4A4_OK;
 }
 
-w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) {
+w4a4_ws_layout ws_layout_of(int64_t T, int64_t k_pad, int64_t k_ld) {
     w4a4_ws_layout w;
     size_t off = 0;
-    w.a_q = off; off = align_up(off + (size_t)(round_up(T, 16) * (d->k_pad / 2)));
-    w.a_s = off; off = align_up(off + (size_t)(T * (d->k_pad / 32)));
-    w.x_o = off; off = align_up(off + (size_t)(T * d->k_ld) * 2);
+    w.a_q = off; off = align_up(off + (size_t)(round_up(T, 16) * (k_pad / 2)));
+    w.a_s = off; off = align_up(off + (size_t)(T * (k_pad / 32)));
+    w.x_o = off; off = align_up(off + (size_t)(T * k_ld) * 2);
     w.total = off;
     return w;
+}
+w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) { return ws_layout_of(T, d->k_pad, d->k_ld); }
+
+// Host half of calibration from the column maxima (bit patterns of max |x| over the
+// calibration tokens and of max |w| over the outputs, per input column):
+// s_j = a^alpha / w^(1-alpha) (sec. 3.2), maxima floored at 1e-5, in double with one
+// rounding; the static top-k of score_j = a_j / s_j (sec. 3.3, scored after the fold
+// per sec. 3.5), larger score first, ties to the smaller column, O ascending.
+int smooth_and_select(const uint32_t* act_bits, const uint32_t* w_bits, int64_t d_in, float alpha, int32_t k,
+                      float* s_out, int32_t* O_out, float* act_scale_out, float* weight_scale_out) {
+    std::vector<float> act((size_t)d_in), wsc((size_t)d_in);
+    for (int64_t j = 0; j < d_in; ++j) {
+        if (act_bits[j] >= 0x7F800000u || w_bits[j] >= 0x7F800000u) return W4A4_ERR_NONFINITE;
+        std::memcpy(&act[j], &act_bits[j], 4);
+        std::memcpy(&wsc[j], &w_bits[j], 4);
+    }
+    const float floor_v = 1e-5f;
+    std::vector<float> score((size_t)d_in);
+    for (int64_t j = 0; j < d_in; ++j) {
+        const float a = act[j] > floor_v ? act[j] : floor_v;
+        const float w = wsc[j] > floor_v ? wsc[j] : floor_v;
+        const double num = std::pow((double)a, (double)alpha);
+        const double den = std::pow((double)w, 1.0 - (double)alpha);
+        s_out[j] = (float)(num / den);
+        score[j] = act[j] / s_out[j];   // = max_t |x_tj / s_j| (binary32 division is monotone)
+    }
+    if (act_scale_out) std::memcpy(act_scale_out, act.data(), (size_t)d_in * 4);
+    if (weight_scale_out) std::memcpy(weight_scale_out, wsc.data(), (size_t)d_in * 4);
+    std::vector<int32_t> idx((size_t)d_in);
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return score[x] > score[y]; });
+    std::sort(idx.begin(), idx.begin() + k);
+    for (int32_t i = 0; i < k; ++i) O_out[i] = idx[i];
+    return W4A4_OK;
+}
+
+// Caller scratch of the alpha / k search: column maxima | packed blob | workspace |
+// reference Y | quantized Y | per-block error sums (sizes for the largest candidate).
+constexpr int kErrBlocks = 512;
+struct SearchLayout {
+    size_t cols, blob, ws, y_ref, y_q, partials, total, blob_bytes, ws_bytes;
+};
+SearchLayout search_layout(int64_t T, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k, int layout) {
+    SearchLayout L;
+    L.blob_bytes = 0;
+    L.ws_bytes = 0;
+    for (int b = 0; b < n_k; ++b) {
+        L.blob_bytes = std::max(L.blob_bytes, blob_layout(d_in, d_out, ks[b], layout).total);
+        const int64_t k_pad = round_up(d_in - ks[b], 128), k_ld = round_up(ks[b], 32);
+        L.ws_bytes = std::max(L.ws_bytes, ws_layout_of(T, k_pad, k_ld).total);
+    }
+    size_t off = 0;
+    L.cols = off;     off = align_up(off + (size_t)d_in * 2 * sizeof(uint32_t));
+    L.blob = off;     off = align_up(off + L.blob_bytes);
+    L.ws = off;       off = align_up(off + L.ws_bytes);
+    L.y_ref = off;    off = align_up(off + (size_t)(T * d_out) * sizeof(float));
+    L.y_q = off;      off = align_up(off + (size_t)(T * d_out) * sizeof(float));
+    L.partials = off; off = align_up(off + (size_t)kErrBlocks * 2 * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+int check_search_args(int64_t T_cal, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k, int layout) {
+    if (!ks || n_k <= 0 || T_cal <= 0) return W4A4_ERR_INVALID;
+    for (int b = 0; b < n_k; ++b) {
+        const int st = check_dims(d_in, d_out, ks[b], layout);
+        if (st) return st;
+    }
+    // the reference kernel's grid has at most 65535 row blocks of 64 tokens
+    if (T_cal > (int64_t)65535 * 64 || T_cal * d_out > ((int64_t)1 << 40)) return W4A4_ERR_SHAPE;
+    return W4A4_OK;
 }
 
 }  // namespace
@@ -133,32 +204,8 @@ int w4a4_calibrate_scales(const void* X_cal, int x_dtype, int64_t T_cal, int64_t
     (void)hipFree(dev);
     if (e != hipSuccess) return W4A4_ERR_DEVICE;
 
-    std::vector<float> act((size_t)d_in), wsc((size_t)d_in);
-    for (int64_t j = 0; j < d_in; ++j) {
-        if (bits[j] >= 0x7F800000u || bits[d_in + j] >= 0x7F800000u) return W4A4_ERR_NONFINITE;
-        std::memcpy(&act[j], &bits[j], 4);
-        std::memcpy(&wsc[j], &bits[d_in + j], 4);
-    }
-    // s_j = a^alpha / w^(1-alpha) (sec. 3.2), maxima floored at 1e-5, double, one rounding.
-    const float floor_v = 1e-5f;
-    std::vector<float> score((size_t)d_in);
-    for (int64_t j = 0; j < d_in; ++j) {
-        const float a = act[j] > floor_v ? act[j] : floor_v;
-        const float w = wsc[j] > floor_v ? wsc[j] : floor_v;
-        const double num = std::pow((double)a, (double)alpha);
-        const double den = std::pow((double)w, 1.0 - (double)alpha);
-        s_out[j] = (float)(num / den);
-        score[j] = act[j] / s_out[j];   // = max_t |x_tj / s_j| (binary32 division is monotone)
-    }
-    if (act_scale_out) std::memcpy(act_scale_out, act.data(), (size_t)d_in * 4);
-    if (weight_scale_out) std::memcpy(weight_scale_out, wsc.data(), (size_t)d_in * 4);
-    // static top-k (sec. 3.3): larger score first, ties to the smaller column
-    std::vector<int32_t> idx((size_t)d_in);
-    std::iota(idx.begin(), idx.end(), 0);
-    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return score[x] > score[y]; });
-    std::sort(idx.begin(), idx.begin() + k);
-    for (int32_t i = 0; i < k; ++i) O_out[i] = idx[i];
-    return W4A4_OK;
+    return smooth_and_select(bits.data(), bits.data() + d_in, d_in, alpha, k, s_out, O_out, act_scale_out,
+                             weight_scale_out);
 }
 
 int w4a4_packed_size(int64_t d_in, int64_t d_out, int32_t k, int layout, size_t* bytes) {
@@ -312,6 +359,83 @@ int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, 
 int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, uint16_t* H,
                           void* ws, size_t ws_bytes, void* stream) {
     return linear_into(X, x_dtype, T, desc, H, true, ws, ws_bytes, stream);
+}
+
+int w4a4_search_scratch_size(int64_t T_cal, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k, int layout,
+                             size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    const int st = check_search_args(T_cal, d_in, d_out, ks, n_k, layout);
+    if (st) return st;
+    *bytes = search_layout(T_cal, d_in, d_out, ks, n_k, layout).total;
+    return W4A4_OK;
+}
+
+int w4a4_search_alpha_k(const void* X_cal, int x_dtype, int64_t T_cal, int64_t d_in, const float* W,
+                        int64_t d_out, const float* alphas, int n_alpha, const int32_t* ks, int n_k, int layout,
+                        void* scratch, size_t scratch_bytes, double* err_out, int32_t* best_out, void* stream) {
+    if (!X_cal || !W || !alphas || n_alpha <= 0 || !scratch || !err_out || !best_out) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    for (int a = 0; a < n_alpha; ++a)
+        if (!(alphas[a] >= 0.0f && alphas[a] <= 1.0f)) return W4A4_ERR_INVALID;
+    int st = check_search_args(T_cal, d_in, d_out, ks, n_k, layout);
+    if (st) return st;
+    if (misaligned(X_cal) || misaligned(W) || misaligned(scratch)) return W4A4_ERR_ALIGN;
+    const SearchLayout L = search_layout(T_cal, d_in, d_out, ks, n_k, layout);
+    if (scratch_bytes < L.total) return W4A4_ERR_SHAPE;
+    hipStream_t hs = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)scratch;
+    uint32_t* cols = (uint32_t*)(base + L.cols);
+    float* y_ref = (float*)(base + L.y_ref);
+    float* y_q = (float*)(base + L.y_q);
+    double* partials = (double*)(base + L.partials);
+    const int64_t n = T_cal * d_out;
+
+    // column maxima once for the whole grid, and the unquantized reference product
+    std::vector<uint32_t> bits((size_t)d_in * 2);
+    hipError_t e = launch_column_absmax(X_cal, x_dtype, T_cal, d_in, cols, hs);
+    if (e == hipSuccess) e = launch_column_absmax(W, W4A4_X_F32, d_out, d_in, cols + d_in, hs);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(bits.data(), cols, bits.size() * sizeof(uint32_t), hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = launch_ref_linear(X_cal, x_dtype, T_cal, d_in, W, d_out, y_ref, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return W4A4_ERR_DEVICE;
+
+    std::vector<float> s((size_t)d_in);
+    std::vector<double> part((size_t)kErrBlocks * 2);
+    best_out[0] = best_out[1] = -1;
+    double best = 0.0;
+    for (int a = 0; a < n_alpha; ++a) {
+        for (int b = 0; b < n_k; ++b) {
+            std::vector<int32_t> O((size_t)ks[b] + 1);
+            st = smooth_and_select(bits.data(), bits.data() + d_in, d_in, alphas[a], ks[b], s.data(), O.data(),
+                                   nullptr, nullptr);
+            if (st) return st;
+            w4a4_packed desc;
+            st = w4a4_pack_weights(W, d_in, d_out, s.data(), O.data(), ks[b], layout, base + L.blob,
+                                   L.blob_bytes, &desc, stream);
+            if (st) return st;
+            st = w4a4_linear(X_cal, x_dtype, T_cal, &desc, y_q, base + L.ws, L.ws_bytes, stream);
+            if (st) return st;
+            e = launch_sq_err(y_q, y_ref, n, partials, kErrBlocks, hs);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(part.data(), partials, part.size() * sizeof(double), hipMemcpyDeviceToHost, hs);
+            if (e == hipSuccess) e = hipStreamSynchronize(hs);
+            if (e != hipSuccess) return W4A4_ERR_DEVICE;
+            double num = 0.0, den = 0.0;
+            for (int i = 0; i < kErrBlocks; ++i) {
+                num += part[2 * i];
+                den += part[2 * i + 1];
+            }
+            const double err = std::sqrt(num / den);
+            err_out[a * n_k + b] = err;
+            if (std::isfinite(err) && (best_out[0] < 0 || err < best)) {
+                best = err;
+                best_out[0] = a;
+                best_out[1] = b;
+            }
+        }
+    }
+    return W4A4_OK;
 }
 
 int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream) {

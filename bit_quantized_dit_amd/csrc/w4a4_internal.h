@@ -22,4 +22,11 @@ hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
 
 hipError_t launch_gelu(const float* Y, int64_t n, uint16_t* H, hipStream_t st);
 
+// alpha / k search: the unquantized fp32 product Y = X W^T, and per-block sums of
+// (Yq - Yr)^2 and Yr^2 (partials[2b], partials[2b + 1])
+hipError_t launch_ref_linear(const void* X, int x_dtype, int64_t T, int64_t d_in, const float* W, int64_t d_out,
+                             float* Y, hipStream_t st);
+hipError_t launch_sq_err(const float* yq, const float* yr, int64_t n, double* partials, int blocks,
+                         hipStream_t st);
+
 }  // namespace w4a4

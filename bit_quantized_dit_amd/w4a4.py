@@ -28,7 +28,8 @@ STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR
 EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", "w4a4_packed_size",
            "w4a4_pack_weights", "w4a4_workspace_layout", "w4a4_workspace_size",
            "w4a4_quantize_activations", "w4a4_gemm_prequantized", "w4a4_linear",
-           "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16")
+           "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16",
+           "w4a4_search_scratch_size", "w4a4_search_alpha_k")
 
 
 class W4A4Packed(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_prequantized_gelu_bf16": (ci, [vp, sz, i64, P(W4A4Packed), vp, vp]),
             "w4a4_linear_gelu_bf16": (ci, [vp, ci, i64, P(W4A4Packed), vp, vp, sz, vp]),
             "w4a4_gelu_tanh_bf16": (ci, [vp, i64, vp, vp]),
+            "w4a4_search_scratch_size": (ci, [i64, i64, i64, vp, ci, ci, P(sz)]),
+            "w4a4_search_alpha_k": (ci, [vp, ci, i64, i64, vp, i64, vp, ci, vp, ci, ci, vp, sz, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -209,6 +212,41 @@ def w4a4_calibrate_scales(X_cal: torch.Tensor, W: torch.Tensor, alpha: float, k:
                                      float(alpha), int(k), vp(s), vp(O), vp(a), vp(w), _stream(stream))
     _check("w4a4_calibrate_scales", st)
     return s, O[:k].copy(), a, w
+
+
+def w4a4_search_scratch_size(T_cal: int, d_in: int, d_out: int, ks, layout: int) -> int:
+    ks_a = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    n = ctypes.c_size_t(0)
+    _check("w4a4_search_scratch_size",
+           lib().w4a4_search_scratch_size(T_cal, d_in, d_out, ks_a.ctypes.data_as(ctypes.c_void_p), ks_a.size,
+                                          layout, ctypes.byref(n)))
+    return n.value
+
+
+def w4a4_search_alpha_k(X_cal: torch.Tensor, W: torch.Tensor, alphas, ks, layout: int, stream=None):
+    """Layer-wise alpha / k search on calibration tokens.  Returns (errors [n_alpha, n_k]
+    as a host float64 array, (a, b) indices of the smallest error); the scratch buffer
+    is allocated here with torch."""
+    _dev(X_cal, "X_cal")
+    _dev(W, "W")
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    T_cal, d_in = X_cal.shape
+    d_out = W.shape[0]
+    if W.shape[1] != d_in:
+        raise ValueError("W must be [d_out, d_in]")
+    al = np.ascontiguousarray(np.asarray(alphas, dtype=np.float32))
+    ka = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    nbytes = w4a4_search_scratch_size(T_cal, d_in, d_out, ka, layout)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=X_cal.device)
+    err = np.zeros(al.size * ka.size, np.float64)
+    best = np.zeros(2, np.int32)
+    vp = lambda arr: arr.ctypes.data_as(ctypes.c_void_p)
+    st = lib().w4a4_search_alpha_k(_ptr(X_cal), _x_dtype(X_cal), T_cal, d_in, _ptr(W), d_out, vp(al), al.size,
+                                   vp(ka), ka.size, layout, _ptr(scratch), nbytes, vp(err), vp(best),
+                                   _stream(stream))
+    _check("w4a4_search_alpha_k", st)
+    return err.reshape(al.size, ka.size), (int(best[0]), int(best[1]))
 
 
 def w4a4_packed_size(d_in: int, d_out: int, k: int, layout: int) -> int:

@@ -175,6 +175,30 @@ int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a
 int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Layer-wise choice of alpha and k (sec. 3.2 gives alpha in [0.5, 0.7] for the FFN up
+ * projection; sec. 4 lists per-layer alpha and k, and sec. 6 names tuning them per
+ * layer as the next step; the pages give no selection rule, so the rule here is the
+ * smallest output error on calibration tokens).  For every pair (alphas[a], ks[b]):
+ * calibrate s and O on X_cal (as w4a4_calibrate_scales), pack W in `layout` (as
+ * w4a4_pack_weights), run the layer on X_cal (as w4a4_linear), and score it by the
+ * relative Frobenius error ||Y_q - Y_ref||_F / ||Y_ref||_F against the unquantized
+ * product Y_ref = X_cal W^T (fp32 inputs and accumulation; the sums of squares in
+ * fp64, added in a fixed order, so the result is deterministic).
+ *   X_cal  device [T_cal][d_in] fp32 or bf16; W device fp32 [d_out][d_in];
+ *   alphas host [n_alpha] in [0,1]; ks host [n_k] in [0,d_in];
+ *   scratch device, scratch_bytes >= w4a4_search_scratch_size (16-byte aligned);
+ *   err_out host [n_alpha * n_k]: err_out[a * n_k + b];
+ *   best_out host [2]: (a, b) of the smallest finite error, first on ties, (-1, -1)
+ *   if none is finite.
+ * Blocking (synchronises `stream` once per candidate); never allocates.  Errors as
+ * the calls it composes (W4A4_ERR_NONFINITE for non-finite calibration data). */
+int w4a4_search_scratch_size(int64_t T_cal, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k,
+                             int layout, size_t* bytes);
+int w4a4_search_alpha_k(const void* X_cal, int x_dtype, int64_t T_cal, int64_t d_in, const float* W,
+                        int64_t d_out, const float* alphas, int n_alpha, const int32_t* ks, int n_k,
+                        int layout, void* scratch, size_t scratch_bytes, double* err_out,
+                        int32_t* best_out, void* stream);
+
 /* The FFN up projection with its activation fused (sec. 3.1 / 3.5: ffn.0 is followed
  * by GELU-tanh, whose bf16 output feeds ffn.2): the dual-branch GEMM of
  * w4a4_gemm_prequantized / w4a4_linear, with every fp32 output y stored as

@@ -293,6 +293,33 @@ def linear(X, s, O, J, packed) -> np.ndarray:
     return output_full(Aq, As, XO, packed)
 
 
+def x_values(X: np.ndarray) -> np.ndarray:
+    """Activation values in fp64: fp32 as is, bf16 bit patterns widened exactly."""
+    if X.dtype == np.uint16:
+        return (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return X.astype(np.float64)
+
+
+def search_alpha_k(X_cal: np.ndarray, W: np.ndarray, alphas, ks, layout: int):
+    """Layer-wise alpha and k ([R] sec. 3.2: alpha in [0.5, 0.7] for the FFN up
+    projection; sec. 4 lists per-layer alpha and k; sec. 6 names tuning them per layer
+    as the next step).  The pages give no selection rule; the one taken is the smallest
+    output error on the calibration tokens: for every (alpha, k), calibrate, pack, run
+    the layer on X_cal and score it by ||Y_q - X_cal W^T||_F / ||X_cal W^T||_F, the
+    reference product in fp64.  Returns (errors [n_alpha, n_k], (a, b) of the smallest
+    error, the first in row-major order on ties)."""
+    Yref = x_values(X_cal) @ np.asarray(W, dtype=np.float64).T
+    nref = np.linalg.norm(Yref)
+    errs = np.empty((len(alphas), len(ks)), dtype=np.float64)
+    for a, alpha in enumerate(alphas):
+        for b, k in enumerate(ks):
+            s, O, J, _, _, _ = calibrate(X_cal, W, float(alpha), int(k))
+            pk = pack_weights(W, s, O, J, layout)
+            errs[a, b] = np.linalg.norm(linear(X_cal, s, O, J, pk) - Yref) / nref
+    a, b = np.unravel_index(int(np.argmin(errs)), errs.shape)
+    return errs, (int(a), int(b))
+
+
 def gelu_bf16(Y: np.ndarray) -> np.ndarray:
     L = _load()
     Y = np.ascontiguousarray(Y, dtype=np.float32)

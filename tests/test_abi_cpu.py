@@ -90,6 +90,33 @@ def test_workspace_layout_is_host_logic(L):
     assert L.w4a4_workspace_size(0, ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
 
 
+def test_search_scratch_size_is_host_logic(L):
+    ks = np.array([0, 16, 64], np.int32)
+    vp = ks.ctypes.data_as(ctypes.c_void_p)
+    n = ctypes.c_size_t(0)
+    assert L.w4a4_search_scratch_size(256, 512, 1024, vp, 3, 0, ctypes.byref(n)) == 0
+    # two fp32 outputs of T_cal x d_out plus the largest candidate's blob, 256-B granules
+    blob = max(B.w4a4_packed_size(512, 1024, int(k), 0) for k in ks)
+    assert n.value >= 2 * 256 * 1024 * 4 + blob and n.value % 256 == 0
+    bad = np.array([0, 600], np.int32)
+    assert L.w4a4_search_scratch_size(256, 512, 1024, bad.ctypes.data_as(ctypes.c_void_p), 2, 0,
+                                      ctypes.byref(n)) == 1                      # k > d_in
+    assert L.w4a4_search_scratch_size(256, 512, 1024, vp, 0, 0, ctypes.byref(n)) == 1   # no candidates
+    assert L.w4a4_search_scratch_size(256, 512, 1024, vp, 3, 7, ctypes.byref(n)) == 1   # bad layout
+    assert L.w4a4_search_scratch_size(65535 * 64 + 1, 512, 1024, vp, 3, 0, ctypes.byref(n)) == 2
+    # the search itself validates before it touches the device
+    al = np.array([0.5, 1.5], np.float32)
+    err = np.zeros(6, np.float64)
+    best = np.zeros(2, np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert L.w4a4_search_alpha_k(ctypes.c_void_p(256), 0, 256, 512, ctypes.c_void_p(256), 1024, p(al), 2, vp, 3,
+                                 0, ctypes.c_void_p(256), 1 << 30, p(err), p(best), None) == 1   # alpha > 1
+    assert L.w4a4_search_alpha_k(ctypes.c_void_p(256), 0, 256, 512, ctypes.c_void_p(256), 1024, p(al), 1, vp, 3,
+                                 0, ctypes.c_void_p(256), 1024, p(err), p(best), None) == 2      # scratch too small
+    assert L.w4a4_search_alpha_k(ctypes.c_void_p(256), 0, 256, 512, ctypes.c_void_p(260), 1024, p(al), 1, vp, 3,
+                                 0, ctypes.c_void_p(256), 1 << 30, p(err), p(best), None) == 3   # misaligned W
+
+
 def test_per_call_entry_points_validate_before_any_launch(L):
     d = _fake_desc()
     n = ctypes.c_size_t(0)

@@ -1,7 +1,7 @@
 """GPU parity of every step of the path against the CPU oracle, through the C ABI.
 
 Codes, scales, the column map, s and O must be bit-exact; Y must meet the output
-tolerance (tests/gpu_util.py).  Shapes span several 128x128 output tiles with ragged
+tolerance (tests/gpu_util.py).  Shapes span several 256x256 output tiles with ragged
 tails in T, d_out, K_J and k, both activation dtypes and all three weight layouts,
 plus the degenerate cases k = 0, k = d_in and special values.
 """
@@ -216,6 +216,29 @@ def test_column_absmax_bits(orc):
     X[10, 7] = np.nan
     out = B.w4a4_column_absmax(to_dev(X))
     assert out.cpu().numpy().view(np.uint32)[7] >= 0x7F800000
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_search_alpha_k_matches_oracle(orc, dt):
+    """The layer-wise alpha / k search: every candidate's error against the oracle's
+    (its calibration, pack and output, and an fp64 reference product), the same choice
+    unless the oracle's best two are within the tolerance of each other, and two runs
+    bitwise equal."""
+    spec = synth.WORKLOADS[1]
+    inp = synth.layer_inputs(spec)
+    Xc, W = inp["X_cal"], inp["W"]
+    if dt == "bf16":
+        Xc = synth.to_bf16_bits(Xc)
+    alphas, ks = [0.5, 0.6, 0.7], [0, 16, 32]
+    _banner(f"alpha/k search {dt} T_cal={Xc.shape[0]} d_in={Xc.shape[1]} d_out={W.shape[0]}")
+    eg, bg = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, 0)
+    eg2, bg2 = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, 0)
+    eo, bo = orc.search_alpha_k(Xc, W, alphas, ks, 0)
+    _banner(f"  gpu {np.array2string(eg, precision=5)} best {bg}; oracle best {bo}")
+    assert np.array_equal(eg, eg2) and bg == bg2
+    np.testing.assert_allclose(eg, eo, rtol=1e-3, atol=0)
+    if bg != bo:
+        assert eo[bg] <= eo[bo] * (1 + 1e-3)
 
 
 def test_calibration_rejects_nonfinite():

@@ -371,6 +371,40 @@ def test_k_equals_din_is_bf16_matmul(orc, mini):
     assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------- alpha / k search
+
+def test_search_k_equals_din_is_the_bf16_error(orc, mini):
+    """With k = d_in every column is an outlier, so each candidate's output is the bf16
+    product whatever alpha is: the search's error must equal the closed form
+    ||bf16(X) bf16(W)^T - X W^T||_F / ||X W^T||_F for every alpha, and the first
+    candidate wins the tie."""
+    rng = np.random.default_rng(21)
+    T, d_in, d_out = 40, 64, 24
+    X = rng.standard_normal((T, d_in)).astype(np.float32)
+    W = (rng.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)
+    errs, best = orc.search_alpha_k(X, W, [0.3, 0.5, 0.9], [d_in], 0)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    q = mini.bf16_to_f64(mini.bf16_bits(X)) @ mini.bf16_to_f64(mini.bf16_bits(W)).T
+    want = np.linalg.norm(q - ref) / np.linalg.norm(ref)
+    assert np.allclose(errs, want, rtol=1e-12, atol=0)
+    assert best == (0, 0)
+
+
+def test_search_prefers_splitting_heavy_columns(orc):
+    """Columns whose magnitude dwarfs the rest inflate their blocks' scales ([R] sec.
+    3.1, 3.3); keeping them in the BF16 branch must lower the output error, and the
+    search must pick the k that covers them."""
+    rng = np.random.default_rng(22)
+    T, d_in, d_out = 64, 128, 32
+    X = (rng.standard_normal((T, d_in)) * 0.3).astype(np.float32)
+    heavy = np.array([5, 40, 77, 120])
+    X[:, heavy] *= 40.0
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    errs, best = orc.search_alpha_k(X, W, [0.5], [0, heavy.size], 0)
+    assert errs[0, 1] < 0.5 * errs[0, 0]
+    assert best == (0, 1)
+
+
 # -------------------------------------------------------------- layouts
 
 @pytest.mark.parametrize("layout", [1, 2])
