@@ -156,6 +156,32 @@ def search_report(Xc, W, layout, alphas=(0.5, 0.6, 0.7), ks=(0, 64, 128, 256)):
             "criterion": "relative Frobenius error of Y on the calibration tokens vs X_cal W^T (fp32)"}
 
 
+def dynamic_report(X, W, s, k, layout, static_us, reps=10):
+    """Per-call outlier selection at the same layer (ungated): the top-k of the call's
+    own column scores instead of the static O, the J branch over all columns.  Times
+    whole w4a4_linear_dyn calls (scores, selection, W_O gather, act-prep, GEMM)."""
+    import torch
+
+    from bit_quantized_dit_amd import w4a4 as B
+
+    pk = B.w4a4_pack_weights_dyn(W, s, k, layout)
+    ws = B.alloc_workspace_dyn(X.shape[0], pk)
+    Y = torch.empty(X.shape[0], W.shape[0], dtype=torch.float32, device=X.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.w4a4_linear_dyn(X, pk, Y, ws, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.w4a4_linear_dyn(X, pk, Y, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del ws, Y, pk
+    return {"k": int(k), "us_per_call": us, "static_us_per_call": static_us, "k_pad": int(X.shape[1] + 127) // 128 * 128}
+
+
 def ffn_block(args):
     """The full FFN block at 57600 tokens: the up projection 5120 -> 13824 (32x32-tile
     weight scales) with GELU-tanh fused into its epilogue (bf16 H), then the down
@@ -359,6 +385,9 @@ def main():
         log("[bench] layer-wise alpha / k search on the calibration tokens (ungated) ...")
         result["search"] = search_report(Xc, W, spec.layout)
         log(f"[bench] search best {result['search']['best']} in {result['search']['ms']:.0f} ms")
+        result["dynamic_outliers"] = dynamic_report(X, W, s, k, spec.layout, (ap_ms + gm_ms) * 1e3)
+        log(f"[bench] per-call outliers: {result['dynamic_outliers']['us_per_call']:.0f} us per call "
+            f"(static {result['dynamic_outliers']['static_us_per_call']:.0f} us)")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(inp, s, O, spec.layout)

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a4.so")
-SOURCES = ["capi.hip", "calib.hip", "pack.hip", "actprep.hip", "gemm.hip", "gelu.hip", "search.hip"]
+SOURCES = ["capi.hip", "calib.hip", "pack.hip", "actprep.hip", "gemm.hip", "gelu.hip", "search.hip", "dynamic.hip"]
 
 # Numerics-relevant flags: IEEE binary32 division, fp32 subnormals kept, no FMA
 # contraction, no fast-math; packed-fp32 instructions disabled.

@@ -151,6 +151,42 @@ SearchLayout search_layout(int64_t T, int64_t d_in, int64_t d_out, const int32_t
     return L;
 }
 
+// Per-call outlier path: the blob is the k = 0 layer's blob followed by W_bf16; the
+// workspace is the k-column layer's (over K_pad = roundup(d_in, 128)) followed by the
+// per-call column maxima, O, column map and W_O.
+int check_dyn_dims(int64_t d_in, int64_t d_out, int32_t k, int layout) {
+    const int st = check_dims(d_in, d_out, k, layout);
+    if (st) return st;
+    if (d_in % 2 != 0 || d_in > W4A4_DYN_MAX_D_IN) return W4A4_ERR_SHAPE;
+    return W4A4_OK;
+}
+size_t dyn_blob_base(int64_t d_in, int64_t d_out, int layout) { return blob_layout(d_in, d_out, 0, layout).total; }
+size_t dyn_blob_total(int64_t d_in, int64_t d_out, int layout) {
+    return dyn_blob_base(d_in, d_out, layout) + align_up((size_t)(d_out * d_in) * 2);
+}
+w4a4_ws_dyn_layout ws_dyn_layout(int64_t T, const w4a4_packed_dyn* d) {
+    w4a4_ws_dyn_layout w;
+    w.base = ws_layout_of(T, d->base.k_pad, round_up(d->k, 32));
+    size_t off = w.base.total;
+    w.colmax = off; off = align_up(off + (size_t)d->base.d_in * 4);
+    w.O = off;      off = align_up(off + (size_t)(d->k > 0 ? d->k : 1) * 4);
+    w.colmap = off; off = align_up(off + (size_t)d->base.d_in * 4);
+    w.W_O = off;    off = align_up(off + (size_t)(d->base.d_out * round_up(d->k, 32)) * 2);
+    w.total = off;
+    return w;
+}
+int check_desc_dyn(const w4a4_packed_dyn* d) {
+    if (!d) return W4A4_ERR_INVALID;
+    int st = check_desc(&d->base);
+    if (st) return st;
+    if (d->base.k != 0) return W4A4_ERR_INVALID;
+    st = check_dyn_dims(d->base.d_in, d->base.d_out, d->k, d->base.layout);
+    if (st) return st;
+    if (!d->W_bf16) return W4A4_ERR_INVALID;
+    if (misaligned(d->W_bf16)) return W4A4_ERR_ALIGN;
+    return W4A4_OK;
+}
+
 int check_search_args(int64_t T_cal, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k, int layout) {
     if (!ks || n_k <= 0 || T_cal <= 0) return W4A4_ERR_INVALID;
     for (int b = 0; b < n_k; ++b) {
@@ -359,6 +395,90 @@ int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, 
 int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, uint16_t* H,
                           void* ws, size_t ws_bytes, void* stream) {
     return linear_into(X, x_dtype, T, desc, H, true, ws, ws_bytes, stream);
+}
+
+int w4a4_packed_dyn_size(int64_t d_in, int64_t d_out, int32_t k, int layout, size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    const int st = check_dyn_dims(d_in, d_out, k, layout);
+    if (st) return st;
+    *bytes = dyn_blob_total(d_in, d_out, layout);
+    return W4A4_OK;
+}
+
+int w4a4_pack_weights_dyn(const float* W, int64_t d_in, int64_t d_out, const float* s, int32_t k, int layout,
+                          void* blob, size_t blob_bytes, w4a4_packed_dyn* desc, void* stream) {
+    if (!W || !s || !blob || !desc) return W4A4_ERR_INVALID;
+    int st = check_dyn_dims(d_in, d_out, k, layout);
+    if (st) return st;
+    if (blob_bytes < dyn_blob_total(d_in, d_out, layout)) return W4A4_ERR_SHAPE;
+    const int32_t no_outliers = 0;
+    st = w4a4_pack_weights(W, d_in, d_out, s, &no_outliers, 0, layout, blob, dyn_blob_base(d_in, d_out, layout),
+                           &desc->base, stream);
+    if (st) return st;
+    uint16_t* wbf = (uint16_t*)((uint8_t*)blob + dyn_blob_base(d_in, d_out, layout));
+    // every column's bf16 weights: the outlier pack with O = J = 0 .. d_in-1
+    const hipError_t e = launch_pack_outliers(W, desc->base.J, d_in, d_out, (int32_t)d_in, d_in, wbf,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return W4A4_ERR_DEVICE;
+    desc->k = k;
+    desc->reserved = 0;
+    desc->W_bf16 = wbf;
+    return W4A4_OK;
+}
+
+int w4a4_workspace_dyn_layout(int64_t T, const w4a4_packed_dyn* desc, w4a4_ws_dyn_layout* out) {
+    if (!out || T < 0) return W4A4_ERR_INVALID;
+    const int st = check_desc_dyn(desc);
+    if (st) return st;
+    *out = ws_dyn_layout(T, desc);
+    return W4A4_OK;
+}
+
+int w4a4_workspace_dyn_size(int64_t T, const w4a4_packed_dyn* desc, size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    w4a4_ws_dyn_layout w;
+    const int st = w4a4_workspace_dyn_layout(T, desc, &w);
+    if (st) return st;
+    *bytes = w.total;
+    return W4A4_OK;
+}
+
+int w4a4_linear_dyn(const void* X, int x_dtype, int64_t T, const w4a4_packed_dyn* desc, float* Y, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (!X || !Y || !ws || T < 0) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    int st = check_desc_dyn(desc);
+    if (st) return st;
+    if (misaligned(X) || misaligned(Y) || misaligned(ws)) return W4A4_ERR_ALIGN;
+    const w4a4_ws_dyn_layout w = ws_dyn_layout(T, desc);
+    if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
+    if (T == 0) return W4A4_OK;
+    hipStream_t hs = (hipStream_t)stream;
+    uint8_t* b = (uint8_t*)ws;
+    const w4a4_packed& base = desc->base;
+    const int64_t k_ld = round_up(desc->k, 32);
+    uint32_t* colmax = (uint32_t*)(b + w.colmax);
+    int32_t* O = (int32_t*)(b + w.O);
+    int32_t* colmap = (int32_t*)(b + w.colmap);
+    uint16_t* W_O = (uint16_t*)(b + w.W_O);
+    hipError_t e = launch_column_absmax(X, x_dtype, T, base.d_in, colmax, hs);
+    if (e == hipSuccess) e = launch_dyn_select(colmax, base.s, base.d_in, desc->k, O, colmap, hs);
+    if (e == hipSuccess) e = launch_dyn_gather(desc->W_bf16, O, base.d_in, base.d_out, desc->k, k_ld, W_O, hs);
+    if (e != hipSuccess) return W4A4_ERR_DEVICE;
+    // The call's layer: every column keeps its K position; act-prep zeroes the J
+    // positions [k_j, k_pad) of its LDS row once per workgroup and never writes the J
+    // position of an outlier column, so k_j = 0 leaves the chosen columns at zero.
+    w4a4_packed d = base;
+    d.k = desc->k;
+    d.k_ld = k_ld;
+    d.k_j = 0;
+    d.colmap = colmap;
+    d.O = O;
+    d.W_O = W_O;
+    e = launch_actprep(X, x_dtype, T, d, b + w.base.a_q, b + w.base.a_s, (uint16_t*)(b + w.base.x_o), hs);
+    if (e == hipSuccess)
+        e = launch_gemm(b + w.base.a_q, b + w.base.a_s, (const uint16_t*)(b + w.base.x_o), T, d, Y, false, hs);
+    return dev_status(e);
 }
 
 int w4a4_search_scratch_size(int64_t T_cal, int64_t d_in, int64_t d_out, const int32_t* ks, int n_k, int layout,

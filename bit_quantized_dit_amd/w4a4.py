@@ -29,7 +29,8 @@ EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", 
            "w4a4_pack_weights", "w4a4_workspace_layout", "w4a4_workspace_size",
            "w4a4_quantize_activations", "w4a4_gemm_prequantized", "w4a4_linear",
            "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16",
-           "w4a4_search_scratch_size", "w4a4_search_alpha_k")
+           "w4a4_search_scratch_size", "w4a4_search_alpha_k", "w4a4_packed_dyn_size", "w4a4_pack_weights_dyn",
+           "w4a4_workspace_dyn_layout", "w4a4_workspace_dyn_size", "w4a4_linear_dyn")
 
 
 class W4A4Packed(ctypes.Structure):
@@ -44,6 +45,16 @@ class W4A4Packed(ctypes.Structure):
 class W4A4WsLayout(ctypes.Structure):
     _fields_ = [("a_q", ctypes.c_size_t), ("a_s", ctypes.c_size_t), ("x_o", ctypes.c_size_t),
                 ("total", ctypes.c_size_t)]
+
+
+class W4A4PackedDyn(ctypes.Structure):
+    _fields_ = [("base", W4A4Packed), ("k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("W_bf16", ctypes.c_void_p)]
+
+
+class W4A4WsDynLayout(ctypes.Structure):
+    _fields_ = [("base", W4A4WsLayout), ("colmax", ctypes.c_size_t), ("O", ctypes.c_size_t),
+                ("colmap", ctypes.c_size_t), ("W_O", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class W4A4Error(RuntimeError):
@@ -82,6 +93,11 @@ def lib() -> ctypes.CDLL:
             "w4a4_gelu_tanh_bf16": (ci, [vp, i64, vp, vp]),
             "w4a4_search_scratch_size": (ci, [i64, i64, i64, vp, ci, ci, P(sz)]),
             "w4a4_search_alpha_k": (ci, [vp, ci, i64, i64, vp, i64, vp, ci, vp, ci, ci, vp, sz, vp, vp, vp]),
+            "w4a4_packed_dyn_size": (ci, [i64, i64, i32, ci, P(sz)]),
+            "w4a4_pack_weights_dyn": (ci, [vp, i64, i64, vp, i32, ci, vp, sz, P(W4A4PackedDyn), vp]),
+            "w4a4_workspace_dyn_layout": (ci, [i64, P(W4A4PackedDyn), P(W4A4WsDynLayout)]),
+            "w4a4_workspace_dyn_size": (ci, [i64, P(W4A4PackedDyn), P(sz)]),
+            "w4a4_linear_dyn": (ci, [vp, ci, i64, P(W4A4PackedDyn), vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -212,6 +228,79 @@ def w4a4_calibrate_scales(X_cal: torch.Tensor, W: torch.Tensor, alpha: float, k:
                                      float(alpha), int(k), vp(s), vp(O), vp(a), vp(w), _stream(stream))
     _check("w4a4_calibrate_scales", st)
     return s, O[:k].copy(), a, w
+
+
+class PackedLayerDyn:
+    """A layer packed for per-call outlier selection: the device blob (kept alive
+    here) and its descriptor."""
+
+    def __init__(self, blob: torch.Tensor, desc: W4A4PackedDyn):
+        self.blob, self.desc = blob, desc
+
+    @property
+    def k(self) -> int: return self.desc.k
+    @property
+    def d_in(self) -> int: return self.desc.base.d_in
+    @property
+    def d_out(self) -> int: return self.desc.base.d_out
+    @property
+    def k_pad(self) -> int: return self.desc.base.k_pad
+
+
+def w4a4_pack_weights_dyn(W: torch.Tensor, s: np.ndarray, k: int, layout: int, stream=None) -> PackedLayerDyn:
+    _dev(W, "W")
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    d_out, d_in = W.shape
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    n = ctypes.c_size_t(0)
+    _check("w4a4_packed_dyn_size", lib().w4a4_packed_dyn_size(d_in, d_out, int(k), int(layout), ctypes.byref(n)))
+    blob = torch.zeros(max(n.value, 256), dtype=torch.uint8, device=W.device)
+    desc = W4A4PackedDyn()
+    st = lib().w4a4_pack_weights_dyn(_ptr(W), d_in, d_out, s.ctypes.data_as(ctypes.c_void_p), int(k), int(layout),
+                                     _ptr(blob), blob.numel(), ctypes.byref(desc), _stream(stream))
+    _check("w4a4_pack_weights_dyn", st)
+    return PackedLayerDyn(blob, desc)
+
+
+def w4a4_workspace_dyn_layout(T: int, packed: PackedLayerDyn) -> W4A4WsDynLayout:
+    out = W4A4WsDynLayout()
+    _check("w4a4_workspace_dyn_layout",
+           lib().w4a4_workspace_dyn_layout(T, ctypes.byref(packed.desc), ctypes.byref(out)))
+    return out
+
+
+def alloc_workspace_dyn(T: int, packed: PackedLayerDyn, device="cuda") -> torch.Tensor:
+    return torch.empty(max(w4a4_workspace_dyn_layout(T, packed).total, 256), dtype=torch.uint8, device=device)
+
+
+def workspace_dyn_views(ws: torch.Tensor, T: int, packed: PackedLayerDyn) -> dict:
+    """Device tensors of one call's per-call state inside ws: O [k], the column map
+    [d_in], W_O [d_out, k_ld], and the quantized activations as workspace_views gives
+    them (over K_pad = roundup(d_in, 128))."""
+    L = w4a4_workspace_dyn_layout(T, packed)
+    k, d_in, d_out = packed.k, packed.d_in, packed.d_out
+    k_ld = (k + 31) // 32 * 32
+    kp = packed.k_pad
+    raw = ws[L.base.a_s:L.base.a_s + T * kp // 32].view(kp // 128, T, 4)
+    rows16 = (T + 15) // 16 * 16
+    aq_raw = ws[L.base.a_q:L.base.a_q + rows16 * kp // 2]
+    return {"O": ws[L.O:L.O + 4 * k].view(torch.int32),
+            "colmap": ws[L.colmap:L.colmap + 4 * d_in].view(torch.int32),
+            "W_O": ws[L.W_O:L.W_O + 2 * d_out * k_ld].view(torch.bfloat16).view(d_out, k_ld),
+            "A_q": untile_codes(aq_raw, rows16, kp)[:T],
+            "A_s": raw.permute(1, 0, 2).reshape(T, kp // 32),
+            "X_O": ws[L.base.x_o:L.base.x_o + T * k_ld * 2].view(torch.bfloat16).view(T, k_ld)}
+
+
+def w4a4_linear_dyn(X: torch.Tensor, packed: PackedLayerDyn, Y: torch.Tensor, ws: torch.Tensor,
+                    stream=None) -> None:
+    _dev(X, "X")
+    _dev(Y, "Y")
+    T = X.shape[0]
+    st = lib().w4a4_linear_dyn(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    _check("w4a4_linear_dyn", st)
 
 
 def w4a4_search_scratch_size(T_cal: int, d_in: int, d_out: int, ks, layout: int) -> int:

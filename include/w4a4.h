@@ -68,6 +68,8 @@ enum {
 /* Largest supported input width (act-prep stages one smoothed row, K_pad fp32,
  * in LDS). */
 #define W4A4_MAX_D_IN 32768
+/* Largest d_in of the per-call outlier path (its top-k sorts the scores in LDS). */
+#define W4A4_DYN_MAX_D_IN 16384
 
 /* Packed layer descriptor, filled by w4a4_pack_weights.  Plain data: copy it
  * freely; it points into the caller's blob and owns nothing. */
@@ -98,6 +100,17 @@ typedef struct w4a4_packed {
 } w4a4_packed;
 
 /* Offsets (bytes) of the quantized activations inside a workspace. */
+/* Layer packed for per-call outlier selection (w4a4_pack_weights_dyn): `base` is the
+ * layer packed over all d_in columns (k = 0: J = every column, s folded in, B_q, B_s,
+ * B_s_rows, B_q_tiles over K_pad = roundup(d_in, 128)); W_bf16 = bf16_rne(W) keeps
+ * every column for the per-call W_O gather; k columns are chosen per call. */
+typedef struct w4a4_packed_dyn {
+    w4a4_packed base;
+    int32_t k;              /* outlier columns chosen per call, 0 <= k <= d_in             */
+    int32_t reserved;
+    const uint16_t* W_bf16; /* device bf16 [d_out][d_in]                                  */
+} w4a4_packed_dyn;
+
 typedef struct w4a4_ws_layout {
     size_t a_q;       /* uint8 activation E2M1 codes in the GEMM's tiled order,
                          [ceil(T/16)][k_pad/128][16][64]: the byte holding codes
@@ -174,6 +187,37 @@ int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a
 /* The per-call path: act-prep then the dual-branch GEMM.  Async; never allocates. */
 int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* Per-call outlier selection, the online variant that sec. 3.3 / sec. 4 attribute to
+ * MixQ and that the page's method replaces with a static top-k.  Each call scores its
+ * own tokens, score_j = fl32(max_t |x_tj| / s_j), compared as binary32 bit patterns of
+ * |score| (numeric order for finite values and +Inf, a NaN above +Inf), larger first,
+ * ties to the smaller column; O = the top k, ascending.  The J branch keeps every
+ * column at its own K position (K_pad = roundup(d_in, 128)) with the chosen columns'
+ * activations set to zero, so its 32-blocks are the column blocks of X rather than
+ * blocks of the compacted J; the O branch is bf16 X_O . bf16 W_O with W_O gathered per
+ * call from W_bf16.  d_in <= W4A4_DYN_MAX_D_IN and even; s as for w4a4_pack_weights.
+ *
+ * w4a4_packed_dyn_size / w4a4_pack_weights_dyn: one device blob (async, like
+ * w4a4_pack_weights).  w4a4_workspace_dyn_layout / _size: for T tokens, the static
+ * workspace of the k-column layer over K_pad = roundup(d_in, 128) followed by the
+ * per-call column maxima (uint32 bit patterns [d_in]), O (int32 [k]), the column map
+ * (int32 [d_in]: j for a J column, -(i+1) for the i-th outlier) and W_O (bf16
+ * [d_out][roundup(k, 32)]).  w4a4_linear_dyn: X device [T][d_in] fp32 or bf16, Y
+ * device fp32 [T][d_out]; async, never allocates; a call reuses its workspace, so
+ * concurrent calls need one each. */
+typedef struct w4a4_ws_dyn_layout {
+    w4a4_ws_layout base;    /* a_q, a_s, x_o as for the static path, k_pad over all columns */
+    size_t colmax, O, colmap, W_O, total;
+} w4a4_ws_dyn_layout;
+int w4a4_packed_dyn_size(int64_t d_in, int64_t d_out, int32_t k, int layout, size_t* bytes);
+int w4a4_pack_weights_dyn(const float* W, int64_t d_in, int64_t d_out, const float* s, int32_t k,
+                          int layout, void* blob, size_t blob_bytes, w4a4_packed_dyn* desc,
+                          void* stream);
+int w4a4_workspace_dyn_layout(int64_t T, const w4a4_packed_dyn* desc, w4a4_ws_dyn_layout* out);
+int w4a4_workspace_dyn_size(int64_t T, const w4a4_packed_dyn* desc, size_t* bytes);
+int w4a4_linear_dyn(const void* X, int x_dtype, int64_t T, const w4a4_packed_dyn* desc, float* Y,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Layer-wise choice of alpha and k (sec. 3.2 gives alpha in [0.5, 0.7] for the FFN up
  * projection; sec. 4 lists per-layer alpha and k, and sec. 6 names tuning them per

@@ -300,6 +300,40 @@ def x_values(X: np.ndarray) -> np.ndarray:
     return X.astype(np.float64)
 
 
+def select_outliers_dynamic(X: np.ndarray, s: np.ndarray, k: int) -> np.ndarray:
+    """Per-call outlier columns (the online selection that [R] sec. 3.3 and sec. 4
+    attribute to MixQ): score_j = fl32(max_t |x_tj| / s_j) on the call's own tokens,
+    ordered by the binary32 bit pattern of |score| (numeric for finite values and +Inf,
+    a NaN above +Inf), larger first, ties to the smaller column; the top k, ascending."""
+    # max_t |x_tj| as the largest |x| bit pattern (the numeric maximum, or a NaN)
+    xb = (X.astype(np.uint32) << 16) if X.dtype == np.uint16 else np.ascontiguousarray(X, np.float32).view(np.uint32)
+    act = (xb & np.uint32(0x7FFFFFFF)).max(axis=0).astype(np.uint32).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        sc = act / np.asarray(s, dtype=np.float32)
+    bits = (sc.view(np.uint32) & np.uint32(0x7FFFFFFF)).astype(np.int64)
+    order = np.lexsort((np.arange(bits.size), -bits))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+def linear_dynamic(X: np.ndarray, W: np.ndarray, s: np.ndarray, k: int, layout: int):
+    """The layer with per-call outliers: O from select_outliers_dynamic; the MXFP4
+    branch keeps every column at its own K position (J = 0..d_in-1, the weights packed
+    once with no outlier column) with the O columns of X set to zero, and the BF16
+    branch is bf16 X_O . bf16 W_O.  Returns (Y, O, A_q, A_s, X_O, W_O)."""
+    d_in = X.shape[1]
+    O = select_outliers_dynamic(X, s, k)
+    J_all = np.arange(d_in, dtype=np.int32)
+    Xz = np.array(X, copy=True)
+    Xz[:, O] = 0
+    Aq, As, _ = act_prep(Xz, s, np.zeros(0, np.int32), J_all)
+    Jc = np.setdiff1d(J_all, O).astype(np.int32)
+    _, _, XO = act_prep(X, s, O, Jc)
+    pk = pack_weights(W, s, np.zeros(0, np.int32), J_all, layout)
+    pk["WO"] = pack_weights(W, s, O, Jc, layout)["WO"]
+    pk["k"] = int(O.size)
+    return output_full(Aq, As, XO, pk), O, Aq, As, XO, pk["WO"]
+
+
 def search_alpha_k(X_cal: np.ndarray, W: np.ndarray, alphas, ks, layout: int):
     """Layer-wise alpha and k ([R] sec. 3.2: alpha in [0.5, 0.7] for the FFN up
     projection; sec. 4 lists per-layer alpha and k; sec. 6 names tuning them per layer

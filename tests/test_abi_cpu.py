@@ -90,6 +90,44 @@ def test_workspace_layout_is_host_logic(L):
     assert L.w4a4_workspace_size(0, ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
 
 
+def test_dynamic_sizes_are_host_logic(L):
+    """Per-call outlier selection: blob and workspace sizes, and the shape rules (d_in
+    even and at most 16384 so one workgroup sorts every column's score)."""
+    n = ctypes.c_size_t(0)
+    assert L.w4a4_packed_dyn_size(512, 1024, 16, 0, ctypes.byref(n)) == 0
+    # the k = 0 blob plus a bf16 copy of W
+    assert n.value >= B.w4a4_packed_size(512, 1024, 0, 0) + 1024 * 512 * 2 and n.value % 256 == 0
+    assert L.w4a4_packed_dyn_size(511, 1024, 16, 0, ctypes.byref(n)) == 2         # odd d_in
+    assert L.w4a4_packed_dyn_size(16386, 1024, 16, 0, ctypes.byref(n)) == 2       # d_in > 16384
+    assert L.w4a4_packed_dyn_size(512, 1024, 513, 0, ctypes.byref(n)) == 1        # k > d_in
+    assert L.w4a4_packed_dyn_size(16384, 64, 16384, 2, ctypes.byref(n)) == 0      # the largest
+    d = B.W4A4PackedDyn()
+    d.base = _fake_desc(k=0)
+    d.k = 40
+    d.W_bf16 = 0x100000
+    out = B.W4A4WsDynLayout()
+    assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 0
+    base = B.W4A4WsLayout()
+    assert L.w4a4_workspace_layout(1000, ctypes.byref(_fake_desc(k=40)), ctypes.byref(base)) == 0
+    # codes over K_pad = roundup(d_in, 128), X_O over k_ld = roundup(k, 32)
+    assert out.base.a_s >= 1008 * 256 and out.base.x_o >= out.base.a_s + 1000 * 16
+    assert out.base.total >= out.base.x_o + 1000 * 64 * 2
+    assert out.colmax >= out.base.total and out.O >= out.colmax + 512 * 4
+    assert out.colmap >= out.O + 40 * 4 and out.W_O >= out.colmap + 512 * 4
+    assert out.total >= out.W_O + 1024 * 64 * 2 and out.total % 256 == 0
+    d.base = _fake_desc(k=16)          # the base blob must hold no static outliers
+    assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 1
+    d.base = _fake_desc(k=0)
+    d.W_bf16 = 0
+    assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 1
+    # the per-call entry point validates before it touches the device
+    d.W_bf16 = 0x100000
+    assert L.w4a4_linear_dyn(ctypes.c_void_p(256), 0, 1000, ctypes.byref(d), ctypes.c_void_p(256),
+                             ctypes.c_void_p(256), 10, None) == 2                  # workspace too small
+    assert L.w4a4_linear_dyn(ctypes.c_void_p(256), 3, 1000, ctypes.byref(d), ctypes.c_void_p(256),
+                             ctypes.c_void_p(256), 1 << 40, None) == 1             # bad dtype
+
+
 def test_search_scratch_size_is_host_logic(L):
     ks = np.array([0, 16, 64], np.int32)
     vp = ks.ctypes.data_as(ctypes.c_void_p)

@@ -218,6 +218,55 @@ def test_column_absmax_bits(orc):
     assert out.cpu().numpy().view(np.uint32)[7] >= 0x7F800000
 
 
+DYN = [
+    # T, d_in, d_out, k, layout, dtype, special values
+    (300, 704, 200, 13, 0, "bf16", False),
+    (129, 1536, 130, 64, 2, "f32", False),
+    (257, 1000, 333, 40, 1, "bf16", True),
+    (64, 512, 96, 0, 0, "bf16", False),
+    (40, 256, 64, 256, 0, "f32", False),      # k = d_in: every column in the BF16 branch
+    (700, 16384, 64, 100, 0, "bf16", False),  # the largest d_in of the per-call path
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,layout,dt,special", DYN)
+def test_dynamic_outliers_match_oracle(orc, T, d_in, d_out, k, layout, dt, special):
+    """Per-call outlier selection: O and the column map exact, the un-compacted codes and
+    scales, X_O and the gathered W_O bit-exact, Y within the output tolerance."""
+    _banner(f"dynamic outliers T={T} d_in={d_in} d_out={d_out} k={k} layout={layout} {dt}")
+    rng = np.random.default_rng(1000 + d_in + k)
+    X = (rng.standard_normal((T, d_in)) * 0.3).astype(np.float32)
+    heavy = rng.choice(d_in, size=min(d_in, 2 * k + 3), replace=False)
+    X[:, heavy] *= rng.uniform(4, 20, heavy.size).astype(np.float32)
+    if special:
+        X[3, heavy[0]] = np.nan
+        X[5, heavy[1]] = -np.inf
+        X[7, 11] = 3e38
+    if dt == "bf16":
+        X = synth.to_bf16_bits(X)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    s = rng.uniform(0.5, 2.0, d_in).astype(np.float32)
+    pk = B.w4a4_pack_weights_dyn(to_dev(W), s, k, layout)
+    ws = B.alloc_workspace_dyn(T, pk)
+    Y = torch.empty(T, d_out, dtype=torch.float32, device="cuda")
+    B.w4a4_linear_dyn(to_dev(X), pk, Y, ws)
+    torch.cuda.synchronize()
+    Yo, O, Aq, As, XO, WO = orc.linear_dynamic(X, W, s, k, layout)
+    v = B.workspace_dyn_views(ws, T, pk)
+    assert np.array_equal(v["O"].cpu().numpy(), O), "O differs"
+    cm = np.arange(d_in, dtype=np.int32)
+    cm[O] = -(np.arange(O.size) + 1)
+    assert np.array_equal(v["colmap"].cpu().numpy(), cm), "column map differs"
+    assert np.array_equal(u8(v["A_s"]), As), "A_s differs"
+    assert np.array_equal(u8(v["A_q"]), Aq), "A_q differs"
+    if k:
+        xo, wo = bf16_bits(v["X_O"]), bf16_bits(v["W_O"])
+        assert np.array_equal(xo[:, :k], XO) and not xo[:, k:].any(), "X_O differs"
+        assert np.array_equal(wo[:, :k], WO) and not wo[:, k:].any(), "W_O differs"
+    st = assert_y_close(Y.cpu().numpy(), Yo)
+    _banner(f"  {st}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_search_alpha_k_matches_oracle(orc, dt):
     """The layer-wise alpha / k search: every candidate's error against the oracle's

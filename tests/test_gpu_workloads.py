@@ -14,7 +14,7 @@ import torch
 from bit_quantized_dit_amd import synth
 from bit_quantized_dit_amd import w4a4 as B
 from tests.gpu_util import (_banner, _check_act, _check_packed, _check_y_full, _layer,
-                            assert_y_close, bf16_bits, to_dev)
+                            assert_y_close, bf16_bits, to_dev, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,6 +146,51 @@ def test_workload5_ffn_block(orc, mini):
     Ysel = Y[torch.as_tensor(drows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
     st = assert_y_close(Ysel.cpu().numpy(), Yref)
     _banner(f"  down: {st}")
+
+
+def test_dynamic_outliers_57600_tokens(orc):
+    """Per-call outlier selection at the full-resolution workload's shape (the launch the
+    benchmark times): O and the column map exact, sampled token rows of the codes and
+    X_O bit-exact, sampled outputs within the tolerance."""
+    spec = synth.WORKLOADS[4]
+    _banner(f"per-call outliers {spec.name}")
+    inp = synth.layer_inputs(spec)
+    X, W = inp["X"], inp["W"]
+    s, _, _, _ = B.w4a4_calibrate_scales(to_dev(inp["X_cal"]), to_dev(W), spec.alpha, spec.k)
+    pk = B.w4a4_pack_weights_dyn(to_dev(W), s, spec.k, spec.layout)
+    T = spec.T
+    ws = B.alloc_workspace_dyn(T, pk)
+    Y = torch.empty(T, W.shape[0], dtype=torch.float32, device="cuda")
+    B.w4a4_linear_dyn(to_dev(X), pk, Y, ws)
+    torch.cuda.synchronize()
+    v = B.workspace_dyn_views(ws, T, pk)
+    O = orc.select_outliers_dynamic(X, s, spec.k)
+    assert np.array_equal(v["O"].cpu().numpy(), O), "O differs"
+    d_in = X.shape[1]
+    cm = np.arange(d_in, dtype=np.int32)
+    cm[O] = -(np.arange(O.size) + 1)
+    assert np.array_equal(v["colmap"].cpu().numpy(), cm), "column map differs"
+    rng = np.random.default_rng(41)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 192)]))
+    Xz = X[rows].copy()
+    Xz[:, O] = 0
+    J_all = np.arange(d_in, dtype=np.int32)
+    Aq_o, As_o, _ = orc.act_prep(Xz, s, np.zeros(0, np.int32), J_all)
+    Jc = np.setdiff1d(J_all, O).astype(np.int32)
+    _, _, XO_o = orc.act_prep(X[rows], s, O, Jc)
+    sel = torch.as_tensor(rows, device="cuda")
+    assert np.array_equal(u8(v["A_s"][sel]), As_o), "A_s differs"
+    assert np.array_equal(u8(v["A_q"][sel]), Aq_o), "A_q differs"
+    assert np.array_equal(bf16_bits(v["X_O"][sel])[:, :spec.k], XO_o), "X_O differs"
+    pk_o = orc.pack_weights(W, s, np.zeros(0, np.int32), J_all, spec.layout)
+    pk_o["WO"] = orc.pack_weights(W, s, O, Jc, spec.layout)["WO"]
+    pk_o["k"] = spec.k
+    N = W.shape[0]
+    ts_l, ns = _sample_pairs(rng, rows.size, N, 4096, full_rows=(0, rows.size - 1))
+    Yref = orc.output_pairs(Aq_o, As_o, XO_o, pk_o, ts_l, ns)
+    Ysel = Y[torch.as_tensor(rows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
+    st = assert_y_close(Ysel.cpu().numpy(), Yref)
+    _banner(f"  {st}")
 
 
 @pytest.mark.parametrize("T,d_in,d_out,k,layout", [(2600, 640, 7001, 24, 0), (2600, 640, 6912, 24, 1),

@@ -405,6 +405,61 @@ def test_search_prefers_splitting_heavy_columns(orc):
     assert best == (0, 1)
 
 
+# --------------------------------------------------------- per-call outliers
+
+def test_dynamic_selection_order_matches_calibration(orc):
+    """For finite scores the bit-pattern order of the per-call selection is the numeric
+    order of the calibration's top-k (larger first, ties to the smaller column)."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((50, 96)).astype(np.float32)
+    X[:, [3, 50]] *= 30.0
+    X[:, 70] = X[:, 3]                      # a tie with column 3
+    s = rng.uniform(0.5, 2.0, 96).astype(np.float32)
+    s[70] = s[3]
+    for k in (0, 1, 2, 3, 17, 96):
+        O, _ = orc.select_outliers(orc.scores(orc.col_absmax(X), s), k)
+        assert np.array_equal(orc.select_outliers_dynamic(X, s, k), O)
+    Xn = X.copy()
+    Xn[0, 10] = np.nan
+    Xn[0, 11] = np.inf
+    assert list(orc.select_outliers_dynamic(Xn, s, 2)) == [10, 11]   # NaN ranks above +Inf
+
+
+def test_dynamic_k_equals_din_is_bf16_matmul(orc, mini):
+    """k = d_in: every column goes to the BF16 branch and the MXFP4 operand is all zero."""
+    rng = np.random.default_rng(32)
+    T, d_in, d_out = 21, 64, 17
+    X = rng.standard_normal((T, d_in)).astype(np.float32)
+    W = (rng.standard_normal((d_out, d_in)) * 0.1).astype(np.float32)
+    s = rng.uniform(0.5, 2, d_in).astype(np.float32)
+    Y, O, Aq, As, XO, WO = orc.linear_dynamic(X, W, s, d_in, 0)
+    assert np.array_equal(O, np.arange(d_in)) and not Aq.any() and not As.any()
+    ref = mini.bf16_to_f64(mini.bf16_bits(X)) @ mini.bf16_to_f64(mini.bf16_bits(W)).T
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_dynamic_chosen_columns_leave_the_fp4_branch(orc, mini):
+    """When only k columns of X are nonzero they are the ones chosen, the MXFP4 branch
+    sees zeros everywhere (all codes and scales 0), and Y is exactly their bf16
+    product; with k = 0 the layer is the static one with no outlier column."""
+    rng = np.random.default_rng(33)
+    T, d_in, d_out = 30, 256, 40
+    cols = np.array([7, 100, 201])
+    X = np.zeros((T, d_in), np.float32)
+    X[:, cols] = rng.standard_normal((T, cols.size)).astype(np.float32)
+    W = (rng.standard_normal((d_out, d_in)) * 0.1).astype(np.float32)
+    s = np.ones(d_in, np.float32)
+    Y, O, Aq, As, XO, WO = orc.linear_dynamic(X, W, s, cols.size, 1)
+    assert np.array_equal(O, cols) and not Aq.any() and not As.any()
+    ref = mini.bf16_to_f64(mini.bf16_bits(X[:, cols])) @ mini.bf16_to_f64(mini.bf16_bits(W[:, cols])).T
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12)
+    X2 = rng.standard_normal((T, d_in)).astype(np.float32)
+    Y0 = orc.linear_dynamic(X2, W, s, 0, 0)[0]
+    J = np.arange(d_in, dtype=np.int32)
+    assert np.array_equal(Y0, orc.linear(X2, s, np.zeros(0, np.int32), J,
+                                         orc.pack_weights(W, s, np.zeros(0, np.int32), J, 0)))
+
+
 # -------------------------------------------------------------- layouts
 
 @pytest.mark.parametrize("layout", [1, 2])
