@@ -151,7 +151,7 @@ SearchLayout search_layout(int64_t T, int64_t d_in, int64_t d_out, const int32_t
     return L;
 }
 
-// Per-call outlier path: the blob is the k = 0 layer's blob followed by W_bf16; the
+// Per-call outlier path: the blob is the k = 0 layer's blob followed by W_t; the
 // workspace is the k-column layer's (over K_pad = roundup(d_in, 128)) followed by the
 // per-call column maxima, O, column map and W_O.
 int check_dyn_dims(int64_t d_in, int64_t d_out, int32_t k, int layout) {
@@ -182,8 +182,8 @@ int check_desc_dyn(const w4a4_packed_dyn* d) {
     if (d->base.k != 0) return W4A4_ERR_INVALID;
     st = check_dyn_dims(d->base.d_in, d->base.d_out, d->k, d->base.layout);
     if (st) return st;
-    if (!d->W_bf16) return W4A4_ERR_INVALID;
-    if (misaligned(d->W_bf16)) return W4A4_ERR_ALIGN;
+    if (!d->W_t) return W4A4_ERR_INVALID;
+    if (misaligned(d->W_t)) return W4A4_ERR_ALIGN;
     return W4A4_OK;
 }
 
@@ -416,13 +416,11 @@ int w4a4_pack_weights_dyn(const float* W, int64_t d_in, int64_t d_out, const flo
                            &desc->base, stream);
     if (st) return st;
     uint16_t* wbf = (uint16_t*)((uint8_t*)blob + dyn_blob_base(d_in, d_out, layout));
-    // every column's bf16 weights: the outlier pack with O = J = 0 .. d_in-1
-    const hipError_t e = launch_pack_outliers(W, desc->base.J, d_in, d_out, (int32_t)d_in, d_in, wbf,
-                                              (hipStream_t)stream);
+    const hipError_t e = launch_dyn_transpose(W, d_in, d_out, wbf, (hipStream_t)stream);
     if (e != hipSuccess) return W4A4_ERR_DEVICE;
     desc->k = k;
     desc->reserved = 0;
-    desc->W_bf16 = wbf;
+    desc->W_t = wbf;
     return W4A4_OK;
 }
 
@@ -463,7 +461,7 @@ int w4a4_linear_dyn(const void* X, int x_dtype, int64_t T, const w4a4_packed_dyn
     uint16_t* W_O = (uint16_t*)(b + w.W_O);
     hipError_t e = launch_column_absmax(X, x_dtype, T, base.d_in, colmax, hs);
     if (e == hipSuccess) e = launch_dyn_select(colmax, base.s, base.d_in, desc->k, O, colmap, hs);
-    if (e == hipSuccess) e = launch_dyn_gather(desc->W_bf16, O, base.d_in, base.d_out, desc->k, k_ld, W_O, hs);
+    if (e == hipSuccess) e = launch_dyn_gather(desc->W_t, O, base.d_in, base.d_out, desc->k, k_ld, W_O, hs);
     if (e != hipSuccess) return W4A4_ERR_DEVICE;
     // The call's layer: every column keeps its K position; act-prep zeroes the J
     // positions [k_j, k_pad) of its LDS row once per workgroup and never writes the J

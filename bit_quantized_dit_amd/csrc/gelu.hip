@@ -1,7 +1,7 @@
 // Standalone GELU-tanh pass between the FFN up projection (ffn.0) and down
 // projection (ffn.2) named in "W4A4 Quantization for Inference on Wan2.2-I2V-A14B
 // (ICME 2026 Challenge)", sec. 3.1 and 3.5:  H = bf16(gelu_tanh(bf16(Y))), element
-// function gelu_tanh_bf16 (w4a4_device.h, shared with the fused GEMM epilogue).
+// function gelu_tanh_bf16x2 (w4a4_device.h, shared with the fused GEMM epilogue).
 // Elementwise and HBM-bound: 8 elements per thread, 32-byte loads, 16-byte stores.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
@@ -15,10 +15,8 @@ __global__ __launch_bounds__(256) void gelu_kernel(const float* __restrict__ Y, 
     if (vec && i0 + 8 <= n) {
         const float4 a = reinterpret_cast<const float4*>(Y + i0)[0];
         const float4 b = reinterpret_cast<const float4*>(Y + i0)[1];
-        const uint32_t w0 = gelu_tanh_bf16(a.x) | ((uint32_t)gelu_tanh_bf16(a.y) << 16);
-        const uint32_t w1 = gelu_tanh_bf16(a.z) | ((uint32_t)gelu_tanh_bf16(a.w) << 16);
-        const uint32_t w2 = gelu_tanh_bf16(b.x) | ((uint32_t)gelu_tanh_bf16(b.y) << 16);
-        const uint32_t w3 = gelu_tanh_bf16(b.z) | ((uint32_t)gelu_tanh_bf16(b.w) << 16);
+        const uint32_t w0 = gelu_tanh_bf16x2(a.x, a.y), w1 = gelu_tanh_bf16x2(a.z, a.w);
+        const uint32_t w2 = gelu_tanh_bf16x2(b.x, b.y), w3 = gelu_tanh_bf16x2(b.z, b.w);
         *reinterpret_cast<uint4*>(H + i0) = make_uint4(w0, w1, w2, w3);
     } else {
         for (int64_t i = i0; i < i0 + 8 && i < n; ++i) H[i] = gelu_tanh_bf16(Y[i]);

@@ -349,26 +349,26 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                     const int64_t t = tl.t0 + wt * 128 + j * 32 + hh * 16 + r;
                     const int64_t n = tl.f0 + wf * 64 + (lane & 15) * 4;
                     if constexpr (GELU) {
-                        const uint32_t h0 = gelu_tanh_bf16(v[0]), h1 = gelu_tanh_bf16(v[1]);
-                        const uint32_t h2 = gelu_tanh_bf16(v[2]), h3 = gelu_tanh_bf16(v[3]);
+                        const uint32_t h01 = gelu_tanh_bf16x2(v[0], v[1]), h23 = gelu_tanh_bf16x2(v[2], v[3]);
                         if (full) {
-                            *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                            *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h01, h23);
                         } else if (t < T) {
                             if (vec_store && n + 3 < N) {
-                                *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                                *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h01, h23);
                             } else {
-                                const uint32_t hv[4] = {h0, h1, h2, h3};
+                                const uint16_t hv[4] = {(uint16_t)h01, (uint16_t)(h01 >> 16), (uint16_t)h23,
+                                                        (uint16_t)(h23 >> 16)};
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
-                                    if (n + e < N) H[t * N + n + e] = (uint16_t)hv[e];
+                                    if (n + e < N) H[t * N + n + e] = hv[e];
                             }
                         }
                     } else {
                         if (full) {
-                            *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                            __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(Y + t * N + n));
                         } else if (t < T) {
                             if (vec_store && n + 3 < N) {
-                                *reinterpret_cast<v4f*>(Y + t * N + n) = v;
+                                __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(Y + t * N + n));
                             } else {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)

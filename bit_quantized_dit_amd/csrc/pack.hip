@@ -151,11 +151,4 @@ hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st) {
     return hipSuccess;
 }
 
-hipError_t launch_pack_outliers(const float* W, const int32_t* O, int64_t d_in, int64_t d_out, int32_t k,
-                                int64_t k_ld, uint16_t* WO, hipStream_t st) {
-    if (d_out * k_ld <= 0) return hipSuccess;
-    pack_outliers_kernel<<<blocks_for(d_out * k_ld), 256, 0, st>>>(W, O, d_in, d_out, k, k_ld, WO);
-    return hipGetLastError();
-}
-
 }  // namespace w4a4

@@ -99,23 +99,40 @@ __device__ __forceinline__ void dma4(v4i srd, uint32_t lds, int voff, int soff) 
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
+// Two binary32 values rounded to bf16, nearest-even, packed (a in the low half):
+// v_cvt_pk_bf16_f32.  On every non-NaN input it equals bf16_rne (all 2^32 patterns
+// compared); a NaN stays a quiet NaN that keeps its top payload bits.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
 // GELU-tanh between the FFN projections ("W4A4 Quantization for Inference on
-// Wan2.2-I2V-A14B (ICME 2026 Challenge)", sec. 3.1 and 3.5) on one fp32 output:
+// Wan2.2-I2V-A14B (ICME 2026 Challenge)", sec. 3.1 and 3.5) on a pair of fp32 outputs:
 // bf16(gelu_tanh(bf16(y))), gelu_tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))),
 // evaluated as x / (1 + exp(-2z)), z = sqrt(2/pi)(x + 0.044715 x^3): the same function
 // (0.5(1 + tanh z) is the logistic of 2z) without the cancellation in 1 + tanh z that
-// wipes out every digit of the negative tail in binary32.  exp and the reciprocal are
-// the hardware v_exp_f32 (2^t) and v_rcp_f32, each within about one binary32 ulp, so
-// the fp32 value is within a few ulps of the exact function before the final rounding
-// to bf16 (8 significant bits).  Tails: x -> -inf gives exp -> inf, rcp -> 0 and a
-// signed zero; x -> +inf gives x.  Shared by the standalone GELU kernel and the GEMM
+// wipes out every digit of the negative tail in binary32.  exp(-2z) = 2^(x (K0 + K1 x^2))
+// with K0 = -2 log2(e) sqrt(2/pi), K1 = 0.044715 K0; exp and the reciprocal are the
+// hardware v_exp_f32 (2^t) and v_rcp_f32, each within about one binary32 ulp, so the
+// fp32 value is within a few ulps of the exact function before the final rounding to
+// bf16 (8 significant bits).  Tails: x -> -inf gives exp -> inf, rcp -> 0 and a signed
+// zero; x -> +inf gives x.  A NaN result (a NaN y, or y = -inf) is written as the quiet
+// NaN 0x7FC0 with the sign of y.  Shared by the standalone GELU kernel and the GEMM
 // epilogue that fuses it, so both give the same bits.
-__device__ __forceinline__ uint16_t gelu_tanh_bf16(float y) {
-    const float x = bf16_to_f32(bf16_rne(y));
-    const float c = 0.7978845608028654f;           // sqrt(2/pi)
-    const float z = c * (x + 0.044715f * x * x * x);
-    const float e = __builtin_amdgcn_exp2f(z * -2.8853900817779268f);   // exp(-2z) = 2^(-2 log2(e) z)
-    return bf16_rne(x * __builtin_amdgcn_rcpf(1.0f + e));
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+    constexpr float K0 = -2.302208198144325f, K1 = -0.1029432395800235f;
+    const float e = __builtin_amdgcn_exp2f(x * __builtin_fmaf(x * x, K1, K0));
+    const float g = x * __builtin_amdgcn_rcpf(1.0f + e);
+    return g != g ? __uint_as_float((__float_as_uint(x) & 0x80000000u) | 0x7FC00000u) : g;
 }
+
+__device__ __forceinline__ uint32_t gelu_tanh_bf16x2(float y0, float y1) {
+    const uint32_t yb = pk_bf16(y0, y1);
+    return pk_bf16(gelu_tanh_f32(__uint_as_float(yb << 16)), gelu_tanh_f32(__uint_as_float(yb & 0xFFFF0000u)));
+}
+
+__device__ __forceinline__ uint16_t gelu_tanh_bf16(float y) { return (uint16_t)gelu_tanh_bf16x2(y, 0.0f); }
 
 }  // namespace w4a4

@@ -33,10 +33,10 @@ hipError_t launch_sq_err(const float* yq, const float* yr, int64_t n, double* pa
 // the W_O gather from the bf16 copy of W
 hipError_t launch_dyn_select(const uint32_t* colmax_bits, const float* s, int64_t d_in, int32_t k, int32_t* O,
                              int32_t* colmap, hipStream_t st);
-hipError_t launch_dyn_gather(const uint16_t* Wbf, const int32_t* O, int64_t d_in, int64_t d_out, int32_t k,
+// W_O[n][i] = W_t[O[i]][n] for i < k, zero for k <= i < k_ld (k_ld a multiple of 32)
+hipError_t launch_dyn_gather(const uint16_t* W_t, const int32_t* O, int64_t d_in, int64_t d_out, int32_t k,
                              int64_t k_ld, uint16_t* WO, hipStream_t st);
-// outlier rows of W (W_O[n][i] = bf16_rne(W[n][O[i]]), zero for i >= k)
-hipError_t launch_pack_outliers(const float* W, const int32_t* O, int64_t d_in, int64_t d_out, int32_t k,
-                                int64_t k_ld, uint16_t* WO, hipStream_t st);
+// W_t[j][n] = bf16_rne(W[n][j]), W fp32 [d_out][d_in]
+hipError_t launch_dyn_transpose(const float* W, int64_t d_in, int64_t d_out, uint16_t* W_t, hipStream_t st);
 
 }  // namespace w4a4

@@ -49,7 +49,7 @@ class W4A4WsLayout(ctypes.Structure):
 
 class W4A4PackedDyn(ctypes.Structure):
     _fields_ = [("base", W4A4Packed), ("k", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("W_bf16", ctypes.c_void_p)]
+                ("W_t", ctypes.c_void_p)]
 
 
 class W4A4WsDynLayout(ctypes.Structure):

@@ -102,13 +102,14 @@ typedef struct w4a4_packed {
 /* Offsets (bytes) of the quantized activations inside a workspace. */
 /* Layer packed for per-call outlier selection (w4a4_pack_weights_dyn): `base` is the
  * layer packed over all d_in columns (k = 0: J = every column, s folded in, B_q, B_s,
- * B_s_rows, B_q_tiles over K_pad = roundup(d_in, 128)); W_bf16 = bf16_rne(W) keeps
- * every column for the per-call W_O gather; k columns are chosen per call. */
+ * B_s_rows, B_q_tiles over K_pad = roundup(d_in, 128)); W_t = bf16_rne(W) transposed
+ * keeps every column of W, contiguous, for the per-call W_O gather; k columns are
+ * chosen per call. */
 typedef struct w4a4_packed_dyn {
     w4a4_packed base;
     int32_t k;              /* outlier columns chosen per call, 0 <= k <= d_in             */
     int32_t reserved;
-    const uint16_t* W_bf16; /* device bf16 [d_out][d_in]                                  */
+    const uint16_t* W_t;    /* device bf16 [d_in][d_out]: W_t[j][n] = bf16_rne(W[n][j])   */
 } w4a4_packed_dyn;
 
 typedef struct w4a4_ws_layout {
@@ -196,7 +197,7 @@ int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, 
  * column at its own K position (K_pad = roundup(d_in, 128)) with the chosen columns'
  * activations set to zero, so its 32-blocks are the column blocks of X rather than
  * blocks of the compacted J; the O branch is bf16 X_O . bf16 W_O with W_O gathered per
- * call from W_bf16.  d_in <= W4A4_DYN_MAX_D_IN and even; s as for w4a4_pack_weights.
+ * call from W_t.  d_in <= W4A4_DYN_MAX_D_IN and even; s as for w4a4_pack_weights.
  *
  * w4a4_packed_dyn_size / w4a4_pack_weights_dyn: one device blob (async, like
  * w4a4_pack_weights).  w4a4_workspace_dyn_layout / _size: for T tokens, the static

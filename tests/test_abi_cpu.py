@@ -104,7 +104,7 @@ def test_dynamic_sizes_are_host_logic(L):
     d = B.W4A4PackedDyn()
     d.base = _fake_desc(k=0)
     d.k = 40
-    d.W_bf16 = 0x100000
+    d.W_t = 0x100000
     out = B.W4A4WsDynLayout()
     assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 0
     base = B.W4A4WsLayout()
@@ -118,10 +118,10 @@ def test_dynamic_sizes_are_host_logic(L):
     d.base = _fake_desc(k=16)          # the base blob must hold no static outliers
     assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 1
     d.base = _fake_desc(k=0)
-    d.W_bf16 = 0
+    d.W_t = 0
     assert L.w4a4_workspace_dyn_layout(1000, ctypes.byref(d), ctypes.byref(out)) == 1
     # the per-call entry point validates before it touches the device
-    d.W_bf16 = 0x100000
+    d.W_t = 0x100000
     assert L.w4a4_linear_dyn(ctypes.c_void_p(256), 0, 1000, ctypes.byref(d), ctypes.c_void_p(256),
                              ctypes.c_void_p(256), 10, None) == 2                  # workspace too small
     assert L.w4a4_linear_dyn(ctypes.c_void_p(256), 3, 1000, ctypes.byref(d), ctypes.c_void_p(256),

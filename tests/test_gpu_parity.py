@@ -206,16 +206,35 @@ def test_fused_gelu_matches_unfused(orc, T, d_in, d_out, k, layout, dt):
     assert bool(torch.equal(Hf.view(torch.int16), H.view(torch.int16)))
 
 
-def test_column_absmax_bits(orc):
-    rng = np.random.default_rng(60)
-    X = (rng.standard_normal((333, 1111)) * rng.uniform(0, 5, 1111)).astype(np.float32)
-    out = B.w4a4_column_absmax(to_dev(X))
+@pytest.mark.parametrize("rows,cols,dt,offset", [
+    (333, 1111, "f32", 0),      # odd column count: super-rows of 4 rows
+    (333, 1111, "bf16", 0),     # super-rows of 8 rows, 5 rows past the last one
+    (1001, 5120, "bf16", 0),    # one row per super-row
+    (77, 6, "f32", 0),          # two rows per super-row, a single workgroup column
+    (5, 3, "bf16", 0),          # fewer rows than one super-row: all element by element
+    (4096, 704, "bf16", 0),
+    (333, 1111, "f32", 1),      # X not 16-byte aligned: the scalar kernel
+])
+def test_column_absmax_bits(orc, rows, cols, dt, offset):
+    """Column max |x| as bit patterns, exact against the oracle; a NaN shows as a
+    pattern at or above +Inf's."""
+    rng = np.random.default_rng(60 + rows + cols)
+    X = (rng.standard_normal((rows, cols)) * rng.uniform(0, 5, cols)).astype(np.float32)
+    X[rows // 2, cols - 1] = -7.5e3
+    Xin = synth.to_bf16_bits(X) if dt == "bf16" else X
+    want = orc.col_absmax(Xin).view(np.uint32)
+    Xd = to_dev(Xin)
+    if offset:
+        flat = torch.empty(rows * cols + offset, dtype=Xd.dtype, device="cuda")
+        flat[offset:] = Xd.reshape(-1)
+        Xd = flat[offset:].view(rows, cols)
+    out = B.w4a4_column_absmax(Xd)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().view(np.float32)
-    assert np.array_equal(got, orc.col_absmax(X))
-    X[10, 7] = np.nan
-    out = B.w4a4_column_absmax(to_dev(X))
-    assert out.cpu().numpy().view(np.uint32)[7] >= 0x7F800000
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+    if dt == "f32" and not offset:
+        X[rows - 1, 0] = np.nan
+        out = B.w4a4_column_absmax(to_dev(X))
+        assert out.cpu().numpy().view(np.uint32)[0] >= 0x7F800000
 
 
 DYN = [
@@ -226,6 +245,8 @@ DYN = [
     (64, 512, 96, 0, 0, "bf16", False),
     (40, 256, 64, 256, 0, "f32", False),      # k = d_in: every column in the BF16 branch
     (700, 16384, 64, 100, 0, "bf16", False),  # the largest d_in of the per-call path
+    (96, 5120, 80, 128, 0, "bf16", "ties"),   # few distinct scores: ties decide the choice
+    (33, 2, 40, 1, 1, "f32", "ties"),         # the smallest d_in
 ]
 
 
@@ -238,14 +259,18 @@ def test_dynamic_outliers_match_oracle(orc, T, d_in, d_out, k, layout, dt, speci
     X = (rng.standard_normal((T, d_in)) * 0.3).astype(np.float32)
     heavy = rng.choice(d_in, size=min(d_in, 2 * k + 3), replace=False)
     X[:, heavy] *= rng.uniform(4, 20, heavy.size).astype(np.float32)
-    if special:
+    s = rng.uniform(0.5, 2.0, d_in).astype(np.float32)
+    if special == "ties":
+        X = rng.choice(np.array([0.0, 0.5, 1.0, 2.0, -3.0], np.float32), size=(T, d_in))
+        X[:, heavy[: k // 2]] *= 4
+        s = np.ones(d_in, np.float32)
+    elif special:
         X[3, heavy[0]] = np.nan
         X[5, heavy[1]] = -np.inf
         X[7, 11] = 3e38
     if dt == "bf16":
         X = synth.to_bf16_bits(X)
     W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
-    s = rng.uniform(0.5, 2.0, d_in).astype(np.float32)
     pk = B.w4a4_pack_weights_dyn(to_dev(W), s, k, layout)
     ws = B.alloc_workspace_dyn(T, pk)
     Y = torch.empty(T, d_out, dtype=torch.float32, device="cuda")
