@@ -54,8 +54,7 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t e2m1_word8(const float* v, uint32_t code) {
     // 2^E, E = code - 127: the biased exponent field, or the subnormal 2^-127 for code 0
     // (code << 23 is at least 2^-126 otherwise, so a maximum selects)
-    const uint32_t sb = code << 23;
-    const float scale = __uint_as_float(sb > 0x00400000u ? sb : 0x00400000u);
+    const float scale = __uint_as_float(__builtin_elementwise_max(code << 23, 0x00400000u));
     uint32_t w = 0;
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
@@ -91,13 +90,15 @@ __device__ __forceinline__ void quantize_row(const float* row, int64_t k_pad, ui
         const float4 a = *reinterpret_cast<const float4*>(src);
         const float4 b = *reinterpret_cast<const float4*>(src + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t q = abs_bits(v[i]);
-            m = q > m ? q : m;
-        }
-        const uint32_t code = e8m0_from_absbits(quad_max_u32(m));
+        // max |v| as IEEE maximum (v_maximum3_f32 with |.| source modifiers): a NaN
+        // propagates, so its bit pattern (positive after |.|) tops every other one
+        const float m01 = __builtin_elementwise_maximum(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+        const float m23 = __builtin_elementwise_maximum(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]));
+        const float m45 = __builtin_elementwise_maximum(__builtin_fabsf(v[4]), __builtin_fabsf(v[5]));
+        const float m67 = __builtin_elementwise_maximum(__builtin_fabsf(v[6]), __builtin_fabsf(v[7]));
+        const float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m01, m23),
+                                                      __builtin_elementwise_maximum(m45, m67));
+        const uint32_t code = e8m0_from_absbits(quad_max_u32(__float_as_uint(m)));
         // converted unconditionally (a NaN/Inf block's scale 2^128 gives some nibbles)
         // and then replaced by zero nibbles, without a branch
         const uint32_t word = e2m1_word8(v, code);
