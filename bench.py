@@ -184,8 +184,11 @@ def dynamic_report(X, W, s, k, layout, static_us, reps=10):
 
 def ffn_block(args):
     """The full FFN block at 57600 tokens: the up projection 5120 -> 13824 (32x32-tile
-    weight scales) with GELU-tanh fused into its epilogue (bf16 H), then the down
-    projection 13824 -> 5120 (128x1 stripes) on H.  One step = both layers."""
+    weight scales) with GELU-tanh and the down layer's activation prep fused into its
+    epilogue (its rows packed in the down layer's J-then-O order), then the down
+    projection 13824 -> 5120 (128x1 stripes).  One step = X -> Y of the block.  The
+    unfused chain (bf16 H written by the up GEMM's GELU epilogue, then a separate
+    act-prep of H) is timed after it for comparison."""
     import torch
 
     from bit_quantized_dit_amd import synth
@@ -202,23 +205,43 @@ def ffn_block(args):
 
     X, Xc, Wu = to_dev(inp["X"]), to_dev(inp["X_cal"]), to_dev(inp["W"])
     s_u, O_u, _, _ = B.w4a4_calibrate_scales(Xc, Wu, up.alpha, up.k)
-    pk_u = B.w4a4_pack_weights(Wu, s_u, O_u, up.layout)
     Wd = to_dev(synth.weights(down, stream=5))
     Xcd = to_dev(synth.down_calibration(inp["X_cal"], inp["W"]))
     s_d, O_d, _, _ = B.w4a4_calibrate_scales(Xcd, Wd, down.alpha, down.k)
     pk_d = B.w4a4_pack_weights(Wd, s_d, O_d, down.layout)
+    P = torch.as_tensor(B.ffn_permutation(O_d, down.d_in), device=dev)
+    pk_u = B.w4a4_pack_weights(Wu[P].contiguous(), s_u, O_u, up.layout)
+    del Wu, Wd
     T = up.T
-    ws_u, ws_d = B.alloc_workspace(T, pk_u), B.alloc_workspace(T, pk_d)
-    H = torch.empty(T, up.d_out, dtype=torch.bfloat16, device=dev)
+    ws_f = B.alloc_workspace_ffn(T, pk_u, pk_d)
+    Lf = B.w4a4_ffn_workspace_layout(T, pk_u, pk_d)
+    ws_fd = ws_f[Lf.down_base:Lf.down_base + Lf.down.total]
     Y = torch.empty(T, down.d_out, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
+        B.w4a4_ffn_forward(X, pk_u, pk_d, Y, ws_f, stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        B.w4a4_ffn_up_quantize(X, pk_u, pk_d, ws_f, stream)
+        ev[i][1].record(stream)
+        B.w4a4_gemm_prequantized(ws_fd, T, pk_d, Y, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    fstage = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e3 for j in range(2)]
+    del ws_f, ws_fd
+    # the unfused chain through the same layers
+    ws_u, ws_d = B.alloc_workspace(T, pk_u), B.alloc_workspace(T, pk_d)
+    H = torch.empty(T, up.d_out, dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
         B.w4a4_linear_gelu_bf16(X, pk_u, H, ws_u, stream)
         B.w4a4_linear(H, pk_d, Y, ws_d, stream)
     torch.cuda.synchronize()
-    K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
         B.w4a4_quantize_activations(X, pk_u, ws_u, stream)
@@ -230,13 +253,14 @@ def ffn_block(args):
         B.w4a4_gemm_prequantized(ws_d, T, pk_d, Y, stream)
         ev[i][4].record(stream)
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / K
     stage = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e3 for j in range(4)]
     flops = 2.0 * T * (up.d_in * up.d_out + down.d_in * down.d_out)
-    log(f"[bench] ffn block: up act-prep {stage[0]:.1f} us, up gemm+gelu {stage[1]:.1f} us, "
-        f"down act-prep {stage[2]:.1f} us, down gemm {stage[3]:.1f} us, step {ms_step:.3f} ms")
-    gemm_flops_up = 2.0 * T * up.d_in * up.d_out
-    achieved = gemm_flops_up / (stage[1] * 1e-6) / 1e12
+    log(f"[bench] ffn block, fused: up act-prep + up gemm (GELU, down act-prep) {fstage[0]:.1f} us, "
+        f"down gemm {fstage[1]:.1f} us, step {ms_step:.3f} ms")
+    log(f"[bench] ffn block, unfused: up act-prep {stage[0]:.1f} us, up gemm+gelu {stage[1]:.1f} us, "
+        f"down act-prep {stage[2]:.1f} us, down gemm {stage[3]:.1f} us, step {sum(stage) * 1e-3:.3f} ms")
+    gemm_flops_down = 2.0 * T * down.d_in * down.d_out
+    achieved = gemm_flops_down / (fstage[1] * 1e-6) / 1e12
     print(json.dumps({
         "metric": "FFN block (W4A4 up + GELU + W4A4 down) TFLOPS, T=57600",
         "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -244,11 +268,12 @@ def ffn_block(args):
         "vs_baseline": None, "dtype": "mxfp4(e2m1/e8m0)+bf16, fp32 accumulate",
         "data": "synthetic (seeded heavy-tailed activations, random weights)",
         "config": {"workload": "ffn_block_T57600_5120x13824x5120", "T": T,
-                   "up_act_prep_us": stage[0], "up_gemm_gelu_us": stage[1],
-                   "down_act_prep_us": stage[2], "down_gemm_us": stage[3]},
-        "roofline": {"bound": "mfma", "kernel": "gemm_w4a4_kernel (up, GELU epilogue)",
+                   "up_quantize_us": fstage[0], "down_gemm_us": fstage[1]},
+        "roofline": {"bound": "mfma", "kernel": "gemm_w4a4_kernel (down)",
                      "achieved": achieved, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP4_TFLOPS, "traffic": None},
+        "unfused": {"up_act_prep_us": stage[0], "up_gemm_gelu_us": stage[1],
+                    "down_act_prep_us": stage[2], "down_gemm_us": stage[3], "step_ms": sum(stage) * 1e-3},
     }), flush=True)
 
 

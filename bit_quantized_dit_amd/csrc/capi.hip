@@ -373,9 +373,90 @@ int linear_into(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, 
     return gemm_into(ws, ws_bytes, T, desc, out, gelu, stream);
 }
 
+w4a4_ffn_ws_layout ffn_layout(int64_t T, const w4a4_packed* up, const w4a4_packed* down) {
+    w4a4_ffn_ws_layout w;
+    w.up = ws_layout(T, up);
+    w.up_base = 0;
+    w.down = ws_layout(T, down);
+    w.down_base = align_up(w.up.total);
+    w.rinv = align_up(w.down_base + w.down.total);
+    w.total = align_up(w.rinv + (size_t)down->k_j * sizeof(double));
+    return w;
+}
+int check_ffn(int64_t T, const w4a4_packed* up, const w4a4_packed* down) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    int st = check_desc(up);
+    if (st) return st;
+    st = check_desc(down);
+    if (st) return st;
+    if (up->d_out != down->d_in) return W4A4_ERR_SHAPE;
+    return W4A4_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int w4a4_ffn_workspace_layout(int64_t T, const w4a4_packed* up, const w4a4_packed* down, w4a4_ffn_ws_layout* out) {
+    if (!out) return W4A4_ERR_INVALID;
+    const int st = check_ffn(T, up, down);
+    if (st) return st;
+    *out = ffn_layout(T, up, down);
+    return W4A4_OK;
+}
+
+int w4a4_ffn_workspace_size(int64_t T, const w4a4_packed* up, const w4a4_packed* down, size_t* bytes) {
+    if (!bytes) return W4A4_ERR_INVALID;
+    w4a4_ffn_ws_layout w;
+    const int st = w4a4_ffn_workspace_layout(T, up, down, &w);
+    if (st) return st;
+    *bytes = w.total;
+    return W4A4_OK;
+}
+
+int w4a4_ffn_up_quantize(const void* X, int x_dtype, int64_t T, const w4a4_packed* up, const w4a4_packed* down,
+                         void* ws, size_t ws_bytes, void* stream) {
+    int st = check_ffn(T, up, down);
+    if (st) return st;
+    if (!X || !ws) return W4A4_ERR_INVALID;
+    if (x_dtype != W4A4_X_F32 && x_dtype != W4A4_X_BF16) return W4A4_ERR_INVALID;
+    if (misaligned(X) || misaligned(ws)) return W4A4_ERR_ALIGN;
+    const w4a4_ffn_ws_layout w = ffn_layout(T, up, down);
+    if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
+    if (T == 0) return W4A4_OK;
+    uint8_t* b = (uint8_t*)ws;
+    st = w4a4_quantize_activations(X, x_dtype, T, up, b + w.up_base, w.up.total, stream);
+    if (st) return st;
+    uint8_t* d = b + w.down_base;
+    QuantDst q;
+    q.aq = d + w.down.a_q;
+    q.as = d + w.down.a_s;
+    q.xo = (uint16_t*)(d + w.down.x_o);
+    q.rinv = (const double*)(b + w.rinv);
+    q.k_j = down->k_j;
+    q.k_pad = down->k_pad;
+    q.k_ld = down->k_ld;
+    q.k = down->k;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = launch_ffn_prologue(*down, T, q, hs);
+    if (e == hipSuccess) {
+        const uint8_t* u = b + w.up_base;
+        e = launch_gemm_quant(u + w.up.a_q, u + w.up.a_s, (const uint16_t*)(u + w.up.x_o), T, *up, q, hs);
+    }
+    return dev_status(e);
+}
+
+int w4a4_ffn_forward(const void* X, int x_dtype, int64_t T, const w4a4_packed* up, const w4a4_packed* down,
+                     float* Y, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_ffn(T, up, down);
+    if (st) return st;
+    if (!Y) return W4A4_ERR_INVALID;
+    if (misaligned(Y)) return W4A4_ERR_ALIGN;
+    st = w4a4_ffn_up_quantize(X, x_dtype, T, up, down, ws, ws_bytes, stream);
+    if (st || T == 0) return st;
+    const w4a4_ffn_ws_layout w = ffn_layout(T, up, down);
+    return gemm_into((uint8_t*)ws + w.down_base, w.down.total, T, down, Y, false, stream);
+}
 
 int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
                            void* stream) {

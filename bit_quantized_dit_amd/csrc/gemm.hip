@@ -95,10 +95,13 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nt_m, uint32_t nt
     tm = first_m + (in_g - tn * gsize);
 }
 
-// GELU = false: out is fp32 Y [T][N].  GELU = true: out is bf16 H [T][N] with
-// H = bf16(gelu_tanh(bf16(Y))) applied to each fp32 output in the epilogue (the FFN
-// up projection feeding the down projection, sec. 3.1 / 3.5), bit-identical to the
-// standalone GELU pass over this kernel's Y.
+// Epilogue variants.  EPI_F32: out is fp32 Y [T][N].  EPI_GELU: out is bf16 H [T][N]
+// with H = bf16(gelu_tanh(bf16(Y))) applied to each fp32 output in the epilogue (the
+// FFN up projection feeding the down projection, sec. 3.1 / 3.5), bit-identical to the
+// standalone GELU pass over this kernel's Y.  EPI_QUANT: H is not stored; the
+// epilogue goes on to the down layer's activation prep of H (sec. 3.2 / 3.3) and
+// writes its A_q, A_s and X_O (QuantDst), bit-identical to the act-prep pass over H.
+constexpr int EPI_F32 = 0, EPI_GELU = 1, EPI_QUANT = 2;
 //
 // Persistent: workgroup b walks the tiles b, b + G, b + 2G, ... of the grouped order
 // (G = grid size, one workgroup per CU; b and b + G sit on the same XCD), and its ring
@@ -106,12 +109,12 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nt_m, uint32_t nt
 // fetch the first steps of the next, whose operands are then in flight while this
 // tile's last MFMAs and its epilogue run.  The refill that the last step would issue
 // waits until the epilogue, which restages the accumulators through that free slot.
-template <bool GELU>
+template <int EPI>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As, const uint16_t* __restrict__ XO,
     int64_t T, const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs_rows,
     const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, void* __restrict__ out,
-    int vec_store) {
+    int vec_store, QuantDst qd) {
     float* __restrict__ Y = reinterpret_cast<float*>(out);
     uint16_t* __restrict__ H = reinterpret_cast<uint16_t*>(out);
     // the ring, then 1 KiB per wavefront that only the null loads of a tile's last
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                     const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
                     const int64_t t = tl.t0 + wt * 128 + j * 32 + hh * 16 + r;
                     const int64_t n = tl.f0 + wf * 64 + (lane & 15) * 4;
-                    if constexpr (GELU) {
+                    if constexpr (EPI == EPI_GELU) {
                         const uint32_t h01 = gelu_tanh_bf16x2(v[0], v[1]), h23 = gelu_tanh_bf16x2(v[2], v[3]);
                         if (full) {
                             *reinterpret_cast<uint2*>(H + t * N + n) = make_uint2(h01, h23);
@@ -378,6 +381,115 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                     }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next half overwrites it
+            }
+        }
+    };
+
+    // Epilogue that quantizes for the down layer.  Each 32-feature MFMA tile of one token
+    // is one 32-block of the down layer's K (f0 and the wavefront's offsets are
+    // multiples of 32): lane l and lane l ^ 32 hold its 16 + 16 values.  Per value
+    // h = bf16(gelu_tanh(bf16(y))) (the pair function the GELU epilogue uses); for a J
+    // position q = fl32(h / s) = fl32(h * RN64(1 / s)) as in act-prep, and positions
+    // past k_j inside the block are zero; the block's E8M0 code comes from the maximum
+    // |q| of both lanes (a NaN propagates and gives 0xFF with zero nibbles); each lane
+    // converts its 16 values into 8 bytes and one exchange with lane ^ 32 (v_perm on the
+    // received word) gives each lane 8 contiguous bytes of the block's 16, stored into
+    // the tiled A_q; lane l < 32 stores the scale byte.  Outlier features (f >= k_j)
+    // store h into X_O.
+    // The tile's 256 reciprocals RN64(1 / s) (zero past k_j) are copied once into the
+    // free ring slot g (every wavefront has finished reading it at the last step's
+    // barrier; its refill waits until after the epilogue), and each lane reads its four
+    // consecutive ones per group q from LDS when it needs them.
+    auto epilogue_quant = [&](const Tile& tl, int g) __attribute__((always_inline)) {
+        const int64_t kj = qd.k_j;
+        const int64_t nkb_d = qd.k_pad / 128;
+        const uint32_t sel_lo = lh ? 0x05040100u : 0x01000504u;
+        const uint32_t sel_hi = lh ? 0x07060302u : 0x03020706u;
+        double* const rs = reinterpret_cast<double*>(smem + (g & (STAGES - 1)) * SLOT_BYTES);
+        if (tid < BF) {
+            const int64_t f = tl.f0 + tid;
+            rs[tid] = f < kj ? qd.rinv[f] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FF; ++i) {
+            const int64_t fb = tl.f0 + wf * 64 + i * 32;   // the block's first feature (wave-uniform)
+            if (fb >= N) continue;
+            const int64_t fl = fb + 4 * lh;                 // lane's features: fl + 8q + e
+            const bool has_j = fb < kj, all_j = fb + 32 <= kj;
+            const double* const rl = rs + (wf * 64 + i * 32 + 4 * lh);   // the lane's fl in the tile
+#pragma unroll
+            for (int j = 0; j < FT; ++j) {
+                const int64_t t = tl.t0 + wt * 128 + j * 32 + l32;
+                const bool tok = t < T;
+                uint32_t hw[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    hw[2 * q] = gelu_tanh_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                    hw[2 * q + 1] = gelu_tanh_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                }
+                if (has_j) {
+                    float qv[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const double4 rq = *reinterpret_cast<const double4*>(rl + 8 * q);
+                        const double rr[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * q + e;
+                            const uint32_t w = hw[r / 2];
+                            const float x = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                            qv[r] = (float)((double)x * rr[e]);
+                            if (!all_j) qv[r] = fl + 8 * q + e < kj ? qv[r] : 0.0f;
+                        }
+                    }
+                    float m4[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        m4[q] = __builtin_elementwise_maximum(
+                            __builtin_elementwise_maximum(__builtin_fabsf(qv[4 * q]), __builtin_fabsf(qv[4 * q + 1])),
+                            __builtin_elementwise_maximum(__builtin_fabsf(qv[4 * q + 2]), __builtin_fabsf(qv[4 * q + 3])));
+                    uint32_t mb = __float_as_uint(__builtin_elementwise_maximum(
+                        __builtin_elementwise_maximum(m4[0], m4[1]), __builtin_elementwise_maximum(m4[2], m4[3])));
+                    const uint32_t pb = (uint32_t)__shfl_xor((int)mb, 32);
+                    mb = pb > mb ? pb : mb;
+                    const uint32_t code = e8m0_from_absbits(mb);
+                    const float scale = __uint_as_float(__builtin_elementwise_max(code << 23, 0x00400000u));
+                    uint32_t p0 = 0, p1 = 0;
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, qv[0], qv[1], scale, 0);
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, qv[2], qv[3], scale, 1);
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, qv[4], qv[5], scale, 2);
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, qv[6], qv[7], scale, 3);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, qv[8], qv[9], scale, 0);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, qv[10], qv[11], scale, 1);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, qv[12], qv[13], scale, 2);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, qv[14], qv[15], scale, 3);
+                    // a NaN/Inf block: zero nibbles
+                    p0 = code == 0xFFu ? 0u : p0;
+                    p1 = code == 0xFFu ? 0u : p1;
+                    // lane < 32 holds bytes {0,1,4,5} / {8,9,12,13} of the block, lane >= 32
+                    // bytes {2,3,6,7} / {10,11,14,15}; after the exchange lane < 32 writes
+                    // bytes 0..7 and lane >= 32 bytes 8..15
+                    const uint32_t own = lh ? p1 : p0;
+                    const uint32_t recv = (uint32_t)__shfl_xor((int)(lh ? p0 : p1), 32);
+                    const uint32_t lo = __builtin_amdgcn_perm(own, recv, sel_lo);
+                    const uint32_t hi = __builtin_amdgcn_perm(own, recv, sel_hi);
+                    if (tok) {
+                        const int r16 = (int)(t & 15);
+                        uint8_t* dst = qd.aq + (((t >> 4) * nkb_d + (fb >> 7)) << 10) + (r16 << 6) +
+                                       (((((int)(fb >> 5)) & 3) ^ (r16 >> 2)) << 4) + lh * 8;
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                        if (lh == 0) qd.as[(((fb >> 7) * T + t) << 2) + ((fb >> 5) & 3)] = (uint8_t)code;
+                    }
+                }
+                if (!all_j && tok) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t f = fl + 8 * (r / 4) + (r % 4);
+                        if (f >= kj && f < N)
+                            qd.xo[t * qd.k_ld + (f - kj)] = (uint16_t)((r & 1) ? (hw[r / 2] >> 16) : hw[r / 2]);
+                    }
+                }
             }
         }
     };
@@ -504,7 +616,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
 
         // The last step's half 1 has already read the next tile's first fragments; they
         // are read again below so that no register holds them across the epilogue.
-        epilogue(cur, base + ns - 1);
+        if constexpr (EPI == EPI_QUANT) epilogue_quant(cur, base + ns - 1);
+        else epilogue(cur, base + ns - 1);
         if (!nxt.valid) break;
         __syncthreads();   // every wavefront is done with the staging slot
         issue(src_of(nxt, STAGES - 1), slot_of(base + ns - 1));
@@ -541,12 +654,59 @@ hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
     // vector stores: 16 bytes (fp32) or 8 bytes (bf16) per lane, aligned when every row is
     const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)out & 15u) == 0);
     const unsigned grid = (unsigned)gemm_grid(tiles);
+    const QuantDst none{};
     if (gelu_bf16)
-        gemm_w4a4_kernel<true><<<dim3(grid), G_THREADS, 0, st>>>(
-            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
+        gemm_w4a4_kernel<EPI_GELU><<<dim3(grid), G_THREADS, 0, st>>>(
+            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, none);
     else
-        gemm_w4a4_kernel<false><<<dim3(grid), G_THREADS, 0, st>>>(
-            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store);
+        gemm_w4a4_kernel<EPI_F32><<<dim3(grid), G_THREADS, 0, st>>>(
+            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
+                             const w4a4_packed& up, const QuantDst& q, hipStream_t st) {
+    if (T <= 0 || up.d_out <= 0) return hipSuccess;
+    const int64_t tiles = ((T + BT - 1) / BT) * ((up.d_out + BF - 1) / BF);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if ((int64_t)BT * (up.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    // the epilogue's 32-blocks are the down layer's: its K is the up layer's N, and its
+    // k_j + k columns are the up layer's outputs
+    if (q.k_j + q.k != up.d_out || q.k_pad % 128 != 0 || q.k_pad < q.k_j) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)gemm_grid(tiles);
+    gemm_w4a4_kernel<EPI_QUANT><<<dim3(grid), G_THREADS, 0, st>>>(
+        Aq, As, XO, T, up.B_q_tiles, up.B_s_rows, up.W_O, up.d_out, up.k_pad, up.k_ld, nullptr, 0, q);
+    return hipGetLastError();
+}
+
+// rinv[p] = RN64(1 / s[J[p]]) for p < k_j (the reciprocal act-prep uses); zero codes
+// and scale bytes for the 32-blocks from ceil(k_j / 32) to k_pad / 32 of every token
+// (the fused epilogue writes the blocks that hold J positions); zero X_O columns
+// k .. k_ld-1 of every token.
+__global__ __launch_bounds__(256) void ffn_prologue_kernel(const float* __restrict__ s, const int32_t* __restrict__ J,
+                                                           int64_t T, QuantDst q) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (int64_t p = g; p < q.k_j; p += stride) const_cast<double*>(q.rinv)[p] = 1.0 / (double)s[J[p]];
+    const int64_t b0 = (q.k_j + 31) / 32, nb = q.k_pad / 32 - b0;   // pad blocks per token
+    const int64_t nkb = q.k_pad / 128;
+    for (int64_t e = g; e < T * nb; e += stride) {
+        const int64_t t = e / nb, b = b0 + e % nb;
+        const int r16 = (int)(t & 15);
+        uint8_t* dst = q.aq + (((t >> 4) * nkb + (b >> 2)) << 10) + (r16 << 6) + ((((int)b & 3) ^ (r16 >> 2)) << 4);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
+        q.as[(((b >> 2) * T + t) << 2) + (b & 3)] = 0;
+    }
+    const int64_t tail = q.k_ld - q.k;
+    for (int64_t e = g; e < T * tail; e += stride) q.xo[(e / tail) * q.k_ld + q.k + e % tail] = 0;
+}
+
+hipError_t launch_ffn_prologue(const w4a4_packed& down, int64_t T, const QuantDst& q, hipStream_t st) {
+    const int64_t work = q.k_j > T * (q.k_pad / 32) ? q.k_j : T * (q.k_pad / 32);
+    if (work <= 0) return hipSuccess;
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    ffn_prologue_kernel<<<(unsigned)blocks, 256, 0, st>>>(down.s, down.J, T, q);
     return hipGetLastError();
 }
 

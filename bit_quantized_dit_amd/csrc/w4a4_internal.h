@@ -17,6 +17,26 @@ hipError_t launch_actprep(const void* X, int x_dtype, int64_t T, const w4a4_pack
                           uint8_t* Aq, uint8_t* As, uint16_t* XO, hipStream_t st);
 
 // out: fp32 Y [T][d_out], or bf16 H = bf16(gelu_tanh(bf16(Y))) when gelu_bf16
+// Destination of the FFN up projection's epilogue that quantizes for the down layer:
+// the down layer's A_q / A_s / X_O (workspace order) and RN64(1 / s_j) of its J columns
+// in compacted order.
+struct QuantDst {
+    uint8_t* aq;
+    uint8_t* as;
+    uint16_t* xo;
+    const double* rinv;
+    int64_t k_j, k_pad, k_ld;
+    int32_t k;
+};
+// Down-layer preparation that the fused epilogue leaves to a separate pass: rinv from
+// the down layer's s and J, zero codes and scales for the 32-blocks past the J columns
+// (up to k_pad), zero X_O columns k .. k_ld-1.
+hipError_t launch_ffn_prologue(const w4a4_packed& down, int64_t T, const QuantDst& q, hipStream_t st);
+// The up projection with GELU and the down layer's activation quantization fused into
+// the epilogue: the up layer's output feature f is the down layer's compacted J
+// position f for f < k_j and its outlier slot f - k_j above.
+hipError_t launch_gemm_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
+                             const w4a4_packed& up, const QuantDst& q, hipStream_t st);
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
                        const w4a4_packed& d, void* out, bool gelu_bf16, hipStream_t st);
 

@@ -30,7 +30,8 @@ EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", 
            "w4a4_quantize_activations", "w4a4_gemm_prequantized", "w4a4_linear",
            "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16",
            "w4a4_search_scratch_size", "w4a4_search_alpha_k", "w4a4_packed_dyn_size", "w4a4_pack_weights_dyn",
-           "w4a4_workspace_dyn_layout", "w4a4_workspace_dyn_size", "w4a4_linear_dyn")
+           "w4a4_workspace_dyn_layout", "w4a4_workspace_dyn_size", "w4a4_linear_dyn",
+           "w4a4_ffn_workspace_layout", "w4a4_ffn_workspace_size", "w4a4_ffn_up_quantize", "w4a4_ffn_forward")
 
 
 class W4A4Packed(ctypes.Structure):
@@ -55,6 +56,11 @@ class W4A4PackedDyn(ctypes.Structure):
 class W4A4WsDynLayout(ctypes.Structure):
     _fields_ = [("base", W4A4WsLayout), ("colmax", ctypes.c_size_t), ("O", ctypes.c_size_t),
                 ("colmap", ctypes.c_size_t), ("W_O", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+class W4A4FfnWsLayout(ctypes.Structure):
+    _fields_ = [("up", W4A4WsLayout), ("down", W4A4WsLayout), ("up_base", ctypes.c_size_t),
+                ("down_base", ctypes.c_size_t), ("rinv", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class W4A4Error(RuntimeError):
@@ -98,6 +104,10 @@ def lib() -> ctypes.CDLL:
             "w4a4_workspace_dyn_layout": (ci, [i64, P(W4A4PackedDyn), P(W4A4WsDynLayout)]),
             "w4a4_workspace_dyn_size": (ci, [i64, P(W4A4PackedDyn), P(sz)]),
             "w4a4_linear_dyn": (ci, [vp, ci, i64, P(W4A4PackedDyn), vp, vp, sz, vp]),
+            "w4a4_ffn_workspace_layout": (ci, [i64, P(W4A4Packed), P(W4A4Packed), P(W4A4FfnWsLayout)]),
+            "w4a4_ffn_workspace_size": (ci, [i64, P(W4A4Packed), P(W4A4Packed), P(sz)]),
+            "w4a4_ffn_up_quantize": (ci, [vp, ci, i64, P(W4A4Packed), P(W4A4Packed), vp, sz, vp]),
+            "w4a4_ffn_forward": (ci, [vp, ci, i64, P(W4A4Packed), P(W4A4Packed), vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -463,3 +473,47 @@ def w4a4_gelu_tanh_bf16(Y: torch.Tensor, H: torch.Tensor, stream=None) -> None:
     _dev(H, "H")
     st = lib().w4a4_gelu_tanh_bf16(_ptr(Y), Y.numel(), _ptr(H), _stream(stream))
     _check("w4a4_gelu_tanh_bf16", st)
+
+
+def ffn_permutation(O_down: np.ndarray, d_ff: int) -> np.ndarray:
+    """Row order of W_up for the fused FFN block: the down layer's J columns
+    (ascending), then its O columns (ascending)."""
+    O = np.sort(np.asarray(O_down, dtype=np.int64))
+    J = np.setdiff1d(np.arange(d_ff), O)
+    return np.concatenate([J, O]).astype(np.int64)
+
+
+def w4a4_ffn_workspace_layout(T: int, up: PackedLayer, down: PackedLayer) -> W4A4FfnWsLayout:
+    out = W4A4FfnWsLayout()
+    _check("w4a4_ffn_workspace_layout",
+           lib().w4a4_ffn_workspace_layout(T, ctypes.byref(up.desc), ctypes.byref(down.desc), ctypes.byref(out)))
+    return out
+
+
+def alloc_workspace_ffn(T: int, up: PackedLayer, down: PackedLayer, device="cuda") -> torch.Tensor:
+    return torch.empty(max(w4a4_ffn_workspace_layout(T, up, down).total, 256), dtype=torch.uint8, device=device)
+
+
+def ffn_workspace_views(ws: torch.Tensor, T: int, up: PackedLayer, down: PackedLayer) -> dict:
+    """The down layer's quantized activations inside an FFN workspace, as
+    workspace_views gives them for a workspace of the down layer alone."""
+    L = w4a4_ffn_workspace_layout(T, up, down)
+    return workspace_views(ws[L.down_base:L.down_base + L.down.total], T, down)
+
+
+def w4a4_ffn_up_quantize(X: torch.Tensor, up: PackedLayer, down: PackedLayer, ws: torch.Tensor, stream=None) -> None:
+    _dev(X, "X")
+    T = X.shape[0]
+    st = lib().w4a4_ffn_up_quantize(_ptr(X), _x_dtype(X), T, ctypes.byref(up.desc), ctypes.byref(down.desc),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    _check("w4a4_ffn_up_quantize", st)
+
+
+def w4a4_ffn_forward(X: torch.Tensor, up: PackedLayer, down: PackedLayer, Y: torch.Tensor, ws: torch.Tensor,
+                     stream=None) -> None:
+    _dev(X, "X")
+    _dev(Y, "Y")
+    T = X.shape[0]
+    st = lib().w4a4_ffn_forward(_ptr(X), _x_dtype(X), T, ctypes.byref(up.desc), ctypes.byref(down.desc), _ptr(Y),
+                                _ptr(ws), ws.numel(), _stream(stream))
+    _check("w4a4_ffn_forward", st)

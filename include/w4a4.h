@@ -220,6 +220,49 @@ int w4a4_workspace_dyn_size(int64_t T, const w4a4_packed_dyn* desc, size_t* byte
 int w4a4_linear_dyn(const void* X, int x_dtype, int64_t T, const w4a4_packed_dyn* desc, float* Y,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* FFN block with the down layer's activation prep fused into the up projection
+ * (sec. 3.1 / 3.5: up projection, GELU-tanh, down projection; sec. 3.2-3.4 for the
+ * down layer's smoothing, outlier split and MXFP4 codes).  H = bf16(gelu_tanh(bf16(
+ * X W_up^T))) never goes to memory: the up GEMM's epilogue writes the down layer's
+ * A_q, A_s and X_O directly, bit-identical to w4a4_quantize_activations(H, down).
+ *
+ * Precondition on the packing: output feature f of `up` must be the down layer's
+ * input column P[f], with P = (the down layer's J columns, ascending, then its O
+ * columns, ascending), i.e. `up` is packed from the rows W_up[P[f]].  Permuting the
+ * rows of W_up does not change its calibration (the per-input-column maxima), and
+ * GELU is elementwise.  With 1x32 or 128x1 weight scales (one row per scale group)
+ * the permuted layer is the same layer with its outputs reordered; with 32x32 tiles
+ * the permutation also regroups the rows that share a tile scale, so the permuted
+ * layer is a different, equally valid quantization of W_up.  The up layer's output
+ * feature f < k_j is the down layer's compacted J position f and f >= k_j its outlier
+ * slot f - k_j.  The library cannot check the permutation.
+ *
+ * w4a4_ffn_workspace_layout / _size: for T tokens, the up layer's workspace (offsets
+ * in `up` relative to up_base), the down layer's (relative to down_base) and
+ * RN64(1 / s_j) of the down layer's J columns (double [down.k_j]).
+ * w4a4_ffn_up_quantize: act-prep of X for `up`, then the up GEMM with GELU and the
+ * down layer's act-prep in its epilogue; afterwards the down layer's A_q, A_s, X_O sit
+ * in the workspace at down_base + down.{a_q, a_s, x_o}, in the layout
+ * w4a4_ws_layout documents.  w4a4_ffn_forward: the same, then the down GEMM into Y
+ * (fp32 [T][down.d_out]).  Errors: INVALID (null pointer, bad dtype, T < 0, a bad
+ * descriptor), SHAPE (up.d_out != down.d_in, workspace too small), ALIGN (pointers
+ * not 16-byte aligned), DEVICE.  Async; never allocates. */
+typedef struct w4a4_ffn_ws_layout {
+    w4a4_ws_layout up;     /* relative to up_base                                   */
+    w4a4_ws_layout down;   /* relative to down_base                                 */
+    size_t up_base, down_base;
+    size_t rinv;           /* double [down.k_j]                                     */
+    size_t total;
+} w4a4_ffn_ws_layout;
+
+int w4a4_ffn_workspace_layout(int64_t T, const w4a4_packed* up, const w4a4_packed* down,
+                              w4a4_ffn_ws_layout* out);
+int w4a4_ffn_workspace_size(int64_t T, const w4a4_packed* up, const w4a4_packed* down, size_t* bytes);
+int w4a4_ffn_up_quantize(const void* X, int x_dtype, int64_t T, const w4a4_packed* up,
+                         const w4a4_packed* down, void* ws, size_t ws_bytes, void* stream);
+int w4a4_ffn_forward(const void* X, int x_dtype, int64_t T, const w4a4_packed* up,
+                     const w4a4_packed* down, float* Y, void* ws, size_t ws_bytes, void* stream);
+
 /* Layer-wise choice of alpha and k (sec. 3.2 gives alpha in [0.5, 0.7] for the FFN up
  * projection; sec. 4 lists per-layer alpha and k, and sec. 6 names tuning them per
  * layer as the next step; the pages give no selection rule, so the rule here is the

@@ -128,6 +128,41 @@ def test_dynamic_sizes_are_host_logic(L):
                              ctypes.c_void_p(256), 1 << 40, None) == 1             # bad dtype
 
 
+def test_ffn_workspace_is_host_logic(L):
+    """The fused FFN block's workspace: the up layer's, then the down layer's, then the
+    down layer's reciprocals; mismatched layers and bad arguments fail before any launch."""
+    up = _fake_desc(d_in=256, d_out=704, k=8)
+    dn = _fake_desc(d_in=704, d_out=256, k=13)
+    out = B.W4A4FfnWsLayout()
+    assert L.w4a4_ffn_workspace_layout(300, ctypes.byref(up), ctypes.byref(dn), ctypes.byref(out)) == 0
+    wu, wd = B.W4A4WsLayout(), B.W4A4WsLayout()
+    assert L.w4a4_workspace_layout(300, ctypes.byref(up), ctypes.byref(wu)) == 0
+    assert L.w4a4_workspace_layout(300, ctypes.byref(dn), ctypes.byref(wd)) == 0
+    assert (out.up.a_q, out.up.a_s, out.up.x_o, out.up.total) == (wu.a_q, wu.a_s, wu.x_o, wu.total)
+    assert (out.down.a_q, out.down.a_s, out.down.x_o, out.down.total) == (wd.a_q, wd.a_s, wd.x_o, wd.total)
+    assert out.up_base == 0 and out.down_base >= wu.total and out.rinv >= out.down_base + wd.total
+    assert out.total >= out.rinv + 8 * (704 - 13) and out.total % 256 == 0 and out.down_base % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert L.w4a4_ffn_workspace_size(300, ctypes.byref(up), ctypes.byref(dn), ctypes.byref(n)) == 0
+    assert n.value == out.total
+    bad = _fake_desc(d_in=640, d_out=256, k=13)     # up.d_out != down.d_in
+    assert L.w4a4_ffn_workspace_size(300, ctypes.byref(up), ctypes.byref(bad), ctypes.byref(n)) == 2
+    assert L.w4a4_ffn_workspace_size(-1, ctypes.byref(up), ctypes.byref(dn), ctypes.byref(n)) == 1
+    p16 = ctypes.c_void_p(256)
+    assert L.w4a4_ffn_forward(p16, 0, 300, ctypes.byref(up), ctypes.byref(dn), p16, p16, 10, None) == 2
+    assert L.w4a4_ffn_forward(p16, 9, 300, ctypes.byref(up), ctypes.byref(dn), p16, p16, 1 << 40, None) == 1
+    assert L.w4a4_ffn_up_quantize(ctypes.c_void_p(258), 0, 300, ctypes.byref(up), ctypes.byref(dn), p16,
+                                  1 << 40, None) == 3
+    # T = 0 is a no-op that touches nothing
+    assert L.w4a4_ffn_forward(p16, 0, 0, ctypes.byref(up), ctypes.byref(dn), p16, p16, 1 << 40, None) == 0
+
+
+def test_ffn_permutation_puts_outliers_last():
+    P = B.ffn_permutation(np.array([40, 3, 17]), 48)
+    assert list(P[-3:]) == [3, 17, 40] and sorted(P) == list(range(48))
+    assert np.all(np.diff(P[:-3]) > 0)
+
+
 def test_search_scratch_size_is_host_logic(L):
     ks = np.array([0, 16, 64], np.int32)
     vp = ks.ctypes.data_as(ctypes.c_void_p)

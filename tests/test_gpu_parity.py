@@ -292,6 +292,65 @@ def test_dynamic_outliers_match_oracle(orc, T, d_in, d_out, k, layout, dt, speci
     _banner(f"  {st}")
 
 
+FFN_FUSED = [
+    # T, d_model, d_ff, k_up, k_down, layout_up, layout_down, dtype, NaN token
+    (300, 256, 704, 8, 13, 0, 2, "bf16", False),   # k_j = 691: one 32-block holds J and O features
+    (129, 512, 1024, 0, 64, 1, 0, "f32", True),    # k_j = 960: two zero pad blocks up to k_pad = 1024
+    (64, 256, 512, 16, 0, 0, 0, "bf16", False),    # no down-layer outliers
+    (257, 384, 640, 4, 128, 2, 1, "bf16", False),  # k_j = 512 = k_pad: no pad
+]
+
+
+@pytest.mark.parametrize("T,d_model,d_ff,k_up,k_down,lu,ld,dt,nan", FFN_FUSED)
+def test_ffn_fused_quantization_matches_unfused(orc, T, d_model, d_ff, k_up, k_down, lu, ld, dt, nan):
+    """The FFN block with the down layer's act-prep in the up GEMM's epilogue: the down
+    layer's A_q, A_s and X_O bit-identical to act-prep of the unfused H (GELU fused
+    into the up GEMM, columns put back in H's order) and to the oracle's act-prep of
+    that H; the down output bit-identical to the down GEMM over the unfused codes."""
+    _banner(f"fused FFN T={T} {d_model}->{d_ff}->{d_model} k_up={k_up} k_down={k_down} {dt}")
+    rng = np.random.default_rng(500 + d_ff + k_down)
+    X = (rng.standard_normal((T, d_model)) * 0.5).astype(np.float32)
+    X[:, rng.choice(d_model, 5, replace=False)] *= 8
+    if nan:
+        X[7, 3] = np.nan
+    Xc = (rng.standard_normal((96, d_model)) * 0.5).astype(np.float32)
+    W_up = (rng.standard_normal((d_ff, d_model)) * 0.05).astype(np.float32)
+    W_dn = (rng.standard_normal((d_model, d_ff)) * 0.05).astype(np.float32)
+    s_up, O_up, _, _ = B.w4a4_calibrate_scales(to_dev(Xc), to_dev(W_up), 0.6, k_up)
+    s_dn = rng.uniform(0.5, 2.0, d_ff).astype(np.float32)
+    O_dn = np.sort(rng.choice(d_ff, k_down, replace=False)).astype(np.int32)
+    P = B.ffn_permutation(O_dn, d_ff)
+    up = B.w4a4_pack_weights(to_dev(W_up[P]), s_up, O_up, lu)
+    down = B.w4a4_pack_weights(to_dev(W_dn), s_dn, O_dn, ld)
+    Xd = to_dev(synth.to_bf16_bits(X) if dt == "bf16" else X)
+    ws = B.alloc_workspace_ffn(T, up, down)
+    ws.fill_(0xA5)        # whatever the fused path leaves unwritten shows up
+    Y = torch.empty(T, d_model, dtype=torch.float32, device="cuda")
+    B.w4a4_ffn_forward(Xd, up, down, Y, ws)
+    fz = B.ffn_workspace_views(ws, T, up, down)
+    # unfused: H in the permuted order, put back in H's column order, then act-prep
+    wsu = B.alloc_workspace(T, up)
+    Hp = torch.empty(T, d_ff, dtype=torch.bfloat16, device="cuda")
+    B.w4a4_linear_gelu_bf16(Xd, up, Hp, wsu)
+    H = torch.empty_like(Hp)
+    H[:, torch.as_tensor(P, device="cuda")] = Hp
+    wsd = B.alloc_workspace(T, down)
+    B.w4a4_quantize_activations(H, down, wsd)
+    rf = B.workspace_views(wsd, T, down)
+    Y2 = torch.empty_like(Y)
+    B.w4a4_gemm_prequantized(wsd, T, down, Y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(fz["A_s"]), u8(rf["A_s"])), "A_s differs"
+    assert np.array_equal(u8(fz["A_q"]), u8(rf["A_q"])), "A_q differs"
+    assert np.array_equal(bf16_bits(fz["X_O"]), bf16_bits(rf["X_O"])), "X_O differs"
+    assert bool(torch.equal(Y.view(torch.int32), Y2.view(torch.int32))), "down output differs"
+    J_dn = np.setdiff1d(np.arange(d_ff), O_dn).astype(np.int32)
+    Aq_o, As_o, XO_o = orc.act_prep(bf16_bits(H), s_dn, O_dn, J_dn)
+    assert np.array_equal(u8(fz["A_s"]), As_o) and np.array_equal(u8(fz["A_q"]), Aq_o)
+    assert np.array_equal(bf16_bits(fz["X_O"])[:, :k_down], XO_o) and not bf16_bits(fz["X_O"])[:, k_down:].any()
+    _banner(f"  codes, scales, X_O and Y identical (NaN rows: {int(np.isnan(Y.cpu().numpy()).any(axis=1).sum())})")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_search_alpha_k_matches_oracle(orc, dt):
     """The layer-wise alpha / k search: every candidate's error against the oracle's

@@ -146,6 +146,37 @@ def test_workload5_ffn_block(orc, mini):
     Ysel = Y[torch.as_tensor(drows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
     st = assert_y_close(Ysel.cpu().numpy(), Yref)
     _banner(f"  down: {st}")
+    # the fully fused block: the down layer's act-prep in the up GEMM's epilogue, the
+    # up layer packed from its rows in the down layer's J-then-O order.  With this
+    # block's 32x32-tile weight scales the row order regroups the shared scales, so the
+    # reference is the unfused chain through the same permuted up layer (GELU fused,
+    # H put back in column order, act-prep, down GEMM).
+    del H, ws, Y, r
+    P = B.ffn_permutation(O, down.d_in)
+    Xd = to_dev(inp["X"])
+    up_p = B.w4a4_pack_weights(to_dev(inp["W"][P]), r_up["s"], r_up["O"], up.layout)
+    wsu = B.alloc_workspace(T, up_p)
+    Hp = torch.empty(T, down.d_in, dtype=torch.bfloat16, device="cuda")
+    B.w4a4_linear_gelu_bf16(Xd, up_p, Hp, wsu)
+    del wsu
+    Hq = torch.empty_like(Hp)
+    Hq[:, torch.as_tensor(P, device="cuda")] = Hp
+    del Hp
+    wsd = B.alloc_workspace(T, packed)
+    B.w4a4_quantize_activations(Hq, packed, wsd)
+    Y2 = torch.empty(T, down.d_out, dtype=torch.float32, device="cuda")
+    B.w4a4_gemm_prequantized(wsd, T, packed, Y2)
+    del Hq
+    wsf = B.alloc_workspace_ffn(T, up_p, packed)
+    Yf = torch.empty_like(Y2)
+    B.w4a4_ffn_forward(Xd, up_p, packed, Yf, wsf)
+    torch.cuda.synchronize()
+    fz, rf = B.ffn_workspace_views(wsf, T, up_p, packed), B.workspace_views(wsd, T, packed)
+    assert bool(torch.equal(fz["A_s"], rf["A_s"])), "fused A_s differs"
+    assert bool(torch.equal(fz["A_q"], rf["A_q"])), "fused A_q differs"
+    assert bool(torch.equal(fz["X_O"].view(torch.int16), rf["X_O"].view(torch.int16))), "fused X_O differs"
+    assert bool(torch.equal(Yf.view(torch.int32), Y2.view(torch.int32))), "fused Y differs"
+    _banner("  fully fused block: down codes, scales, X_O and Y identical to the unfused chain")
 
 
 def test_dynamic_outliers_57600_tokens(orc):
