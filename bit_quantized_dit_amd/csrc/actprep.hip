@@ -218,8 +218,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     const XT* __restrict__ X, int64_t T, int64_t d_in, const int32_t* __restrict__ colmap,
     const float* __restrict__ s, int64_t k_j, int64_t k_pad, int32_t k, int64_t k_ld,
     uint8_t* __restrict__ Aq, uint8_t* __restrict__ As, uint16_t* __restrict__ XO) {
-    extern __shared__ float row[];
-    zero_pads<NT>(row, k_j, k_pad, k, k_ld);
+    // two LDS row buffers: row r is staged in buffer r % 2, so phase 1 of the next row
+    // needs no barrier behind phase 2 of this one (a wavefront writes buffer r % 2 for
+    // row r + 2 only after passing row r + 1's barrier, which every wavefront reaches
+    // after finishing phase 2 of row r)
+    extern __shared__ float lds_rows[];
+    const int64_t row_words = lds_words(k_pad, k_ld);
+    zero_pads<NT>(lds_rows, k_j, k_pad, k, k_ld);
+    zero_pads<NT>(lds_rows + row_words, k_j, k_pad, k, k_ld);
 
     const int64_t npairs = d_in / 2;
     int32_t slot[MAXM][2];
@@ -266,6 +272,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
         for (int d = 0; d < D; ++d) {
             const int64_t t = t_begin + r0 + d;
             if (t >= t_end) break;
+            float* const row = lds_rows + ((r0 + d) & 1) * row_words;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 const float lo = Pair<XT>::lo(xv[d][m]), hi = Pair<XT>::hi(xv[d][m]);
@@ -279,7 +286,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
             __syncthreads();
             quantize_row<NT>(row, k_pad, Aq, t, As + t * 4, T * 4);
             copy_outliers<NT>(row, k_pad, k_ld, XO + t * k_ld);
-            __syncthreads();
         }
     };
     raw xa[D][MAXM], xb[D][MAXM];
@@ -309,19 +315,20 @@ static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uin
     }
     const int64_t resident = (n <= 2 * (int64_t)AP_THREADS * 8) ? 2 * (int64_t)cus[dev] : (int64_t)cus[dev];
     const unsigned grid = (unsigned)(T < resident ? T : resident);
-#define W4A4_AP_LAUNCH(KERNEL, NT)                                                                   \
+#define W4A4_AP_LAUNCH(KERNEL, NT, LDS)                                                              \
     {                                                                                                \
-        if (lds > 65536) {                                                                           \
+        const size_t lds_b = (LDS);                                                                  \
+        if (lds_b > 65536) {                                                                         \
             hipError_t e = hipFuncSetAttribute((const void*)KERNEL,                                  \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_b); \
             if (e != hipSuccess) return e;                                                           \
         }                                                                                            \
-        KERNEL<<<grid, NT, lds, st>>>(X, T, d.d_in, d.colmap, d.s, d.k_j, d.k_pad, d.k, d.k_ld, Aq, \
-                                      As, XO);                                                       \
+        KERNEL<<<grid, NT, lds_b, st>>>(X, T, d.d_in, d.colmap, d.s, d.k_j, d.k_pad, d.k, d.k_ld, Aq, \
+                                        As, XO);                                                     \
         return hipGetLastError();                                                                    \
     }
 #define W4A4_AP_PAIRS(NT, M) \
-    if (n % 2 == 0 && n <= 2 * (int64_t)(NT) * (M)) W4A4_AP_LAUNCH((actprep_pairs_kernel<XT, NT, M>), NT)
+    if (n % 2 == 0 && n <= 2 * (int64_t)(NT) * (M)) W4A4_AP_LAUNCH((actprep_pairs_kernel<XT, NT, M>), NT, 2 * lds)
     W4A4_AP_PAIRS(512, 1)
     W4A4_AP_PAIRS(512, 2)
     W4A4_AP_PAIRS(512, 3)
@@ -334,7 +341,7 @@ static hipError_t launch_typed(const XT* X, int64_t T, const w4a4_packed& d, uin
     W4A4_AP_PAIRS(1024, 6)
     W4A4_AP_PAIRS(1024, 7)
     W4A4_AP_PAIRS(1024, 8)
-    W4A4_AP_LAUNCH((actprep_kernel<XT>), AP_THREADS)
+    W4A4_AP_LAUNCH((actprep_kernel<XT>), AP_THREADS, lds)
 #undef W4A4_AP_PAIRS
 #undef W4A4_AP_LAUNCH
 }
