@@ -65,10 +65,11 @@ enum {
     W4A4_WS_128X1_STRIPE = 2   /* B_s [d_out][K_pad/128]: 128 K x 1 row, K-major stripes      */
 };
 
-/* Largest supported input width (act-prep stages one smoothed row, K_pad fp32,
+/* Largest supported input width (act-prep stages smoothed rows, K_pad fp32 each,
  * in LDS). */
 #define W4A4_MAX_D_IN 32768
-/* Largest d_in of the per-call outlier path (its top-k sorts the scores in LDS). */
+/* Largest d_in of the per-call outlier path (its top-k holds every column's score
+ * in the registers of one 1024-lane workgroup, 16 per lane). */
 #define W4A4_DYN_MAX_D_IN 16384
 
 /* Packed layer descriptor, filled by w4a4_pack_weights.  Plain data: copy it
