@@ -25,6 +25,9 @@ SMALL = [
     (129, 1536, 130, 64, 2, "f32"),     # 128x1 stripes
     (64, 5120, 256, 128, 0, "bf16"),    # K_J = 4992: odd number of 128-steps
     (1, 512, 64, 16, 2, "bf16"),
+    (77, 333, 96, 5, 0, "f32"),         # odd d_in: the generic act-prep kernel
+    (45, 333, 70, 7, 1, "bf16"),        # odd d_in, bf16 rows at odd element offsets
+    (40, 20000, 64, 16, 0, "bf16"),     # d_in beyond the fast act-prep paths (16384)
 ]
 
 
