@@ -294,7 +294,7 @@ def main():
                          "many MiB (the known-size kernel that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); the layer shards by tokens with no exchange, "
               f"so per-GPU throughput is the single-GPU figure.", file=sys.stderr)
         sys.exit(2)
