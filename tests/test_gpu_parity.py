@@ -250,6 +250,7 @@ DYN = [
     (700, 16384, 64, 100, 0, "bf16", False),  # the largest d_in of the per-call path
     (96, 5120, 80, 128, 0, "bf16", "ties"),   # few distinct scores: ties decide the choice
     (33, 2, 40, 1, 1, "f32", "ties"),         # the smallest d_in
+    (1, 512, 64, 8, 2, "bf16", False),        # a single token
 ]
 
 
@@ -301,6 +302,8 @@ FFN_FUSED = [
     (129, 512, 1024, 0, 64, 1, 0, "f32", True),    # k_j = 960: two zero pad blocks up to k_pad = 1024
     (64, 256, 512, 16, 0, 0, 0, "bf16", False),    # no down-layer outliers
     (257, 384, 640, 4, 128, 2, 1, "bf16", False),  # k_j = 512 = k_pad: no pad
+    (70, 256, 700, 6, 12, 0, 0, "bf16", False),    # d_ff = 700: the block at 672 holds J, O and
+                                                   # columns past d_ff
 ]
 
 
@@ -354,8 +357,8 @@ def test_ffn_fused_quantization_matches_unfused(orc, T, d_model, d_ff, k_up, k_d
     _banner(f"  codes, scales, X_O and Y identical (NaN rows: {int(np.isnan(Y.cpu().numpy()).any(axis=1).sum())})")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_search_alpha_k_matches_oracle(orc, dt):
+@pytest.mark.parametrize("dt,layout", [("f32", 0), ("bf16", 0), ("bf16", 1), ("f32", 2)])
+def test_search_alpha_k_matches_oracle(orc, dt, layout):
     """The layer-wise alpha / k search: every candidate's error against the oracle's
     (its calibration, pack and output, and an fp64 reference product), the same choice
     unless the oracle's best two are within the tolerance of each other, and two runs
@@ -366,10 +369,10 @@ def test_search_alpha_k_matches_oracle(orc, dt):
     if dt == "bf16":
         Xc = synth.to_bf16_bits(Xc)
     alphas, ks = [0.5, 0.6, 0.7], [0, 16, 32]
-    _banner(f"alpha/k search {dt} T_cal={Xc.shape[0]} d_in={Xc.shape[1]} d_out={W.shape[0]}")
-    eg, bg = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, 0)
-    eg2, bg2 = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, 0)
-    eo, bo = orc.search_alpha_k(Xc, W, alphas, ks, 0)
+    _banner(f"alpha/k search {dt} layout={layout} T_cal={Xc.shape[0]} d_in={Xc.shape[1]} d_out={W.shape[0]}")
+    eg, bg = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, layout)
+    eg2, bg2 = B.w4a4_search_alpha_k(to_dev(Xc), to_dev(W), alphas, ks, layout)
+    eo, bo = orc.search_alpha_k(Xc, W, alphas, ks, layout)
     _banner(f"  gpu {np.array2string(eg, precision=5)} best {bg}; oracle best {bo}")
     assert np.array_equal(eg, eg2) and bg == bg2
     np.testing.assert_allclose(eg, eo, rtol=1e-3, atol=0)
