@@ -4,11 +4,13 @@
 // scales after the fold and the column extraction, 32x32 tiles or 128x1 K-major
 // stripes, exponent stored beside the 4-bit payload).
 //
-// W arrives in nn.Linear orientation [d_out][d_in] (K contiguous).  The folded J
-// weights w'[n][p] = fl32(s[J[p]] * W[n][J[p]]) are never materialised: pass 1
-// computes one E8M0 code per scale group, pass 2 recomputes w' per 32-element
-// chunk and writes 16 bytes of nibbles.  Both passes are gathers through J and run
-// once per layer, so they favour plainness over bandwidth.
+// W arrives in nn.Linear orientation [d_out][d_in] (K contiguous).  For the row-local
+// layouts (1x32, 128x1 stripes) one workgroup packs one row: the folded J weights
+// w'[p] = fl32(s[J[p]] * W[n][J[p]]) are staged in LDS at their compacted positions
+// (a coalesced pass over the row), then each lane quantizes 8 consecutive positions.
+// For 32x32 tiles, whose groups span 32 rows, pass 1 computes one E8M0 code per group
+// and pass 2 recomputes w' per 32-element chunk and writes 16 bytes of nibbles; both
+// are gathers through J that favour plainness over bandwidth.
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
 
@@ -110,6 +112,80 @@ __global__ __launch_bounds__(256) void pack_row_scales_kernel(const uint8_t* __r
     Bs_rows[((kb / 4) * d_out + n) * 4 + (kb % 4)] = c;
 }
 
+// LDS word of compacted position p: 16 bytes of padding after every 32 positions, so
+// that the 16-byte reads of consecutive lanes (32 bytes apart) spread over the banks.
+__device__ __forceinline__ int32_t pack_lds_pos(int64_t p) { return (int32_t)(p + ((p >> 5) << 2)); }
+
+// Row-local layouts: one 256-lane workgroup per row n of roundup(d_out, 16) (rows past
+// d_out only zero their part of the tiled copy).  Lane i takes positions 8i + 2048m:
+// the block maximum over |w'| (IEEE maximum, so a NaN propagates; a 32-block is a quad
+// of lanes, a 128-stripe 16 lanes), the E8M0 code from its exponent field, and the
+// nibbles from four scaled FP4 conversions (nearest even, saturating at 6, divisor
+// 2^E; a NaN/Inf group gets zero nibbles).  Writes B_q, its tiled copy, B_s and the
+// step-major B_s_rows directly.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const float* __restrict__ W, const float* __restrict__ s,
+                                                        const int32_t* __restrict__ colmap, int64_t d_in,
+                                                        int64_t d_out, int64_t k_j, int64_t k_pad, int layout,
+                                                        uint8_t* __restrict__ Bq, uint8_t* __restrict__ Bqt,
+                                                        uint8_t* __restrict__ Bs, uint8_t* __restrict__ Bs_rows) {
+    extern __shared__ float wrow[];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nkb128 = k_pad / 128;
+    if (n >= d_out) {
+        for (int64_t p0 = (int64_t)tid * 8; p0 < k_pad; p0 += 256 * 8)
+            *reinterpret_cast<uint32_t*>(Bqt + tiled_chunk(n, p0 >> 7, nkb128, (int)((p0 >> 5) & 3)) +
+                                         ((p0 & 31) >> 1)) = 0u;
+        return;
+    }
+    const float* wr = W + n * d_in;
+    for (int64_t j = tid; j < d_in; j += 256) {
+        const int32_t m = colmap[j];
+        if (m >= 0) wrow[pack_lds_pos(m)] = s[j] * wr[j];   // one binary32 multiply
+    }
+    for (int64_t p = k_j + tid; p < k_pad; p += 256) wrow[pack_lds_pos(p)] = 0.0f;
+    __syncthreads();
+    const bool stripe = layout == W4A4_WS_128X1_STRIPE;
+    for (int64_t p0 = (int64_t)tid * 8; p0 < k_pad; p0 += 256 * 8) {
+        const float* src = wrow + pack_lds_pos(p0);
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const float m01 = __builtin_elementwise_maximum(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+        const float m23 = __builtin_elementwise_maximum(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]));
+        const float m45 = __builtin_elementwise_maximum(__builtin_fabsf(v[4]), __builtin_fabsf(v[5]));
+        const float m67 = __builtin_elementwise_maximum(__builtin_fabsf(v[6]), __builtin_fabsf(v[7]));
+        uint32_t mb = __float_as_uint(__builtin_elementwise_maximum(__builtin_elementwise_maximum(m01, m23),
+                                                                    __builtin_elementwise_maximum(m45, m67)));
+        // the 32-block: lanes 4q .. 4q+3
+        uint32_t o = (uint32_t)__shfl_xor((int)mb, 1);
+        mb = o > mb ? o : mb;
+        o = (uint32_t)__shfl_xor((int)mb, 2);
+        mb = o > mb ? o : mb;
+        if (stripe) {   // the 128-stripe: lanes 16r .. 16r+15
+            o = (uint32_t)__shfl_xor((int)mb, 4);
+            mb = o > mb ? o : mb;
+            o = (uint32_t)__shfl_xor((int)mb, 8);
+            mb = o > mb ? o : mb;
+        }
+        const uint32_t code = e8m0_from_absbits(mb);
+        const float scale = __uint_as_float(__builtin_elementwise_max(code << 23, 0x00400000u));
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+        w = code == 0xFFu ? 0u : w;
+        *reinterpret_cast<uint32_t*>(Bq + n * (k_pad / 2) + (p0 >> 1)) = w;
+        *reinterpret_cast<uint32_t*>(Bqt + tiled_chunk(n, p0 >> 7, nkb128, (int)((p0 >> 5) & 3)) + ((p0 & 31) >> 1)) = w;
+        if ((p0 & 31) == 0) {
+            Bs_rows[((p0 >> 7) * d_out + n) * 4 + ((p0 >> 5) & 3)] = (uint8_t)code;
+            if (!stripe) Bs[n * (k_pad / 32) + (p0 >> 5)] = (uint8_t)code;
+            else if ((p0 & 127) == 0) Bs[n * nkb128 + (p0 >> 7)] = (uint8_t)code;
+        }
+    }
+}
+
 // Outlier rows in bf16, raw (unsmoothed), zero padded to k_ld.
 __global__ __launch_bounds__(256) void pack_outliers_kernel(const float* __restrict__ W,
                                                             const int32_t* __restrict__ O, int64_t d_in,
@@ -124,7 +200,21 @@ __global__ __launch_bounds__(256) void pack_outliers_kernel(const float* __restr
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 hipError_t launch_pack(const float* W, const w4a4_packed& d, hipStream_t st) {
-    if (d.k_pad > 0) {
+    if (d.k_pad > 0 && (d.layout == W4A4_WS_1X32 || d.layout == W4A4_WS_128X1_STRIPE)) {
+        const size_t lds = (size_t)(d.k_pad + d.k_pad / 8) * sizeof(float);
+        if (lds > 65536) {
+            const hipError_t e = hipFuncSetAttribute((const void*)pack_rows_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        const int64_t rows = (d.d_out + 15) / 16 * 16;
+        if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+        pack_rows_kernel<<<(unsigned)rows, 256, lds, st>>>(W, d.s, d.colmap, d.d_in, d.d_out, d.k_j, d.k_pad,
+                                                           d.layout, (uint8_t*)d.B_q, (uint8_t*)d.B_q_tiles,
+                                                           (uint8_t*)d.B_s, (uint8_t*)d.B_s_rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (d.k_pad > 0) {
         int64_t groups;
         if (d.layout == W4A4_WS_1X32) groups = d.d_out * (d.k_pad / 32);
         else if (d.layout == W4A4_WS_128X1_STRIPE) groups = d.d_out * (d.k_pad / 128);
