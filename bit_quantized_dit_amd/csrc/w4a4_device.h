@@ -29,24 +29,6 @@ __device__ __forceinline__ uint32_t e8m0_from_absbits(uint32_t amax_bits) {
     return e == 0xFFu ? 0xFFu : c;
 }
 
-// 2^-E as a binary32 for a finite scale code c (c <= 252 for finite amax, so the
-// biased exponent 254 - c stays in [2, 254]).
-__device__ __forceinline__ float e8m0_inverse(uint32_t c) { return __uint_as_float((254u - c) << 23); }
-
-// E2M1 nibble of x under the inverse scale `inv` (a power of two, so |x| * inv is
-// exact whenever it is a normal number; below 2^-126 every rounding gives code 0).
-__device__ __forceinline__ uint32_t e2m1_nibble(float x, float inv) {
-    const float m = __builtin_fabsf(x) * inv;
-    uint32_t c = (m > 0.25f) ? 1u : 0u;
-    c += (m >= 0.75f) ? 1u : 0u;
-    c += (m > 1.25f) ? 1u : 0u;
-    c += (m >= 1.75f) ? 1u : 0u;
-    c += (m > 2.5f) ? 1u : 0u;
-    c += (m >= 3.5f) ? 1u : 0u;
-    c += (m > 5.0f) ? 1u : 0u;
-    return c | ((__float_as_uint(x) >> 28) & 8u);
-}
-
 // binary32 -> bf16, round to nearest even; a NaN becomes the canonical quiet NaN
 // with its sign kept.
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
