@@ -36,6 +36,10 @@
  *     aligned; buffers sized by the size queries are 256-byte aligned inside.
  *   - Calls on different streams that share a workspace race; the library keeps
  *     no global state and is otherwise reentrant.
+ *   - The async per-call entry points enqueue kernels only: no allocation, no
+ *     memset or copy, no synchronisation (memory that must start at zero is
+ *     cleared by a kernel).  They may be captured into a HIP graph once the same
+ *     call has run eagerly on the device (the first call sets kernel attributes).
  */
 #ifndef W4A4_H
 #define W4A4_H
@@ -200,8 +204,8 @@ int w4a4_linear(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, 
  * blocks of the compacted J; the O branch is bf16 X_O . bf16 W_O with W_O gathered per
  * call from W_t.  d_in <= W4A4_DYN_MAX_D_IN and even; s as for w4a4_pack_weights.
  *
- * w4a4_packed_dyn_size / w4a4_pack_weights_dyn: one device blob (async, like
- * w4a4_pack_weights).  w4a4_workspace_dyn_layout / _size: for T tokens, the static
+ * w4a4_packed_dyn_size / w4a4_pack_weights_dyn: one device blob (blocking,
+ * like w4a4_pack_weights).  w4a4_workspace_dyn_layout / _size: for T tokens, the static
  * workspace of the k-column layer over K_pad = roundup(d_in, 128) followed by the
  * per-call column maxima (uint32 bit patterns [d_in]), O (int32 [k]), the column map
  * (int32 [d_in]: j for a J column, -(i+1) for the i-th outlier) and W_O (bf16
