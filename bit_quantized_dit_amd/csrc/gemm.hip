@@ -273,7 +273,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         v4i b[FF], a[FT];          // 16 bytes per operand (32 FP4 codes or 8 bf16)
     };
     struct Scales {
-        uint32_t b[FF], a[FT];     // raw scale words of a step; the lane's byte is selected at use
+        uint32_t b[FF], a[FT];     // scale words of a step (shifted in place at first use)
     };
     // g is the ring index of the step (its slot is g % STAGES)
     auto load_b = [&](Frags& f, int g, int h, int i) __attribute__((always_inline)) {
@@ -293,6 +293,12 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         if (o < FF) c.b[o] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[wf * 64 + o * 32 + l32];
         else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * 128 + (o - FF) * 32 + l32];
     };
+    // A row's scale word holds the E8M0 bytes of its four 32-blocks of the step, and lane
+    // l feeds block 2h + l/32 in half-step h.  Each word is shifted right by 8 * (l / 32)
+    // in place just before its first MFMA of the step (the wait for its LDS read falls
+    // there anyway); the block's byte is then byte 2h, which the MFMA selects by
+    // immediate: one shift per word and step instead of one per word and half-step.
+    const int lsh = 8 * lh;
     auto load_half = [&](Frags& f, int g, int h, int o) __attribute__((always_inline)) {   // o-th of 6 operand reads
         if (o < FF) load_b(f, g, h, o);
         else load_a(f, g, h, o - FF);
@@ -307,13 +313,17 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     };
-    // one MFMA of a half-step; sh selects the lane's E8M0 byte of the scale words
+    // one MFMA of a half-step; the scale operands' byte select 2h picks the lane's E8M0
+    // byte of the pre-shifted scale words
     auto mma_fp4 = [&](const Frags& f, const Scales& c, int h, int i, int j) __attribute__((always_inline)) {
-        const int sh = 8 * (2 * h + lh);
         const v8i b = v8i{f.b[i][0], f.b[i][1], f.b[i][2], f.b[i][3], 0, 0, 0, 0};
         const v8i a = v8i{f.a[j][0], f.a[j][1], f.a[j][2], f.a[j][3], 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            b, a, acc[i][j], 4, 4, 0, (int)(c.b[i] >> sh), 0, (int)(c.a[j] >> sh));
+        if (h == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 4, 4, 0, (int)c.b[i], 0,
+                                                                          (int)c.a[j]);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 4, 4, 2, (int)c.b[i], 2,
+                                                                          (int)c.a[j]);
     };
     auto mma_bf16 = [&](const Frags& f, int i, int j) __attribute__((always_inline)) {
         const v8bf wb = __builtin_bit_cast(v8bf, f.b[i]);
@@ -574,10 +584,12 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         // FP4 steps, unrolled by two so that the scale words of the current and the
         // next step alternate between c0 and c1 without a copy (a copy would wait for
         // every outstanding LDS read at the end of each step)
-        auto fp4_step = [&](int st, const Scales& cs, Scales& nx, bool fast) __attribute__((always_inline)) {
+        auto fp4_step = [&](int st, Scales& cs, Scales& nx, bool fast) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NM; ++s) {
+                if (s < FF) cs.b[s] >>= lsh;
+                if (s % FF == 0) cs.a[s / FF] >>= lsh;
                 mma_fp4(f0, cs, 0, s % FF, s / FF);
                 if (s < FF + FT) load_half(f1, base + st, 1, s);
                 __builtin_amdgcn_sched_barrier(0);
