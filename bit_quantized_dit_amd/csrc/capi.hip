@@ -81,16 +81,17 @@ int check_desc(const w4a4_packed* d) {
     return W4A4_OK;
 }
 
-w4a4_ws_layout ws_layout_of(int64_t T, int64_t k_pad, int64_t k_ld) {
+w4a4_ws_layout ws_layout_of(int64_t T, int64_t d_out, int64_t k_pad, int64_t k_ld) {
     w4a4_ws_layout w;
     size_t off = 0;
-    w.a_q = off; off = align_up(off + (size_t)(round_up(T, 16) * (k_pad / 2)));
-    w.a_s = off; off = align_up(off + (size_t)(T * (k_pad / 32)));
-    w.x_o = off; off = align_up(off + (size_t)(T * k_ld) * 2);
+    w.a_q = off;     off = align_up(off + (size_t)(round_up(T, 16) * (k_pad / 2)));
+    w.a_s = off;     off = align_up(off + (size_t)(T * (k_pad / 32)));
+    w.x_o = off;     off = align_up(off + (size_t)(T * k_ld) * 2);
+    w.partial = off; off = align_up(off + gemm_split_plan(T, d_out, k_pad, k_ld).part_bytes);
     w.total = off;
     return w;
 }
-w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) { return ws_layout_of(T, d->k_pad, d->k_ld); }
+w4a4_ws_layout ws_layout(int64_t T, const w4a4_packed* d) { return ws_layout_of(T, d->d_out, d->k_pad, d->k_ld); }
 
 // Host half of calibration from the column maxima (bit patterns of max |x| over the
 // calibration tokens and of max |w| over the outputs, per input column):
@@ -138,7 +139,7 @@ SearchLayout search_layout(int64_t T, int64_t d_in, int64_t d_out, const int32_t
     for (int b = 0; b < n_k; ++b) {
         L.blob_bytes = std::max(L.blob_bytes, blob_layout(d_in, d_out, ks[b], layout).total);
         const int64_t k_pad = round_up(d_in - ks[b], 128), k_ld = round_up(ks[b], 32);
-        L.ws_bytes = std::max(L.ws_bytes, ws_layout_of(T, k_pad, k_ld).total);
+        L.ws_bytes = std::max(L.ws_bytes, ws_layout_of(T, d_out, k_pad, k_ld).total);
     }
     size_t off = 0;
     L.cols = off;     off = align_up(off + (size_t)d_in * 2 * sizeof(uint32_t));
@@ -166,7 +167,7 @@ size_t dyn_blob_total(int64_t d_in, int64_t d_out, int layout) {
 }
 w4a4_ws_dyn_layout ws_dyn_layout(int64_t T, const w4a4_packed_dyn* d) {
     w4a4_ws_dyn_layout w;
-    w.base = ws_layout_of(T, d->base.k_pad, round_up(d->k, 32));
+    w.base = ws_layout_of(T, d->base.d_out, d->base.k_pad, round_up(d->k, 32));
     size_t off = w.base.total;
     w.colmax = off; off = align_up(off + (size_t)d->base.d_in * 4);
     w.O = off;      off = align_up(off + (size_t)(d->k > 0 ? d->k : 1) * 4);
@@ -345,7 +346,7 @@ int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_
 
 namespace {
 
-int gemm_into(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, void* out, bool gelu,
+int gemm_into(void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, void* out, bool gelu,
               void* stream) {
     if (T < 0) return W4A4_ERR_INVALID;
     int st = check_desc(desc);
@@ -355,8 +356,9 @@ int gemm_into(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* des
     if (misaligned(ws) || misaligned(out)) return W4A4_ERR_ALIGN;
     const w4a4_ws_layout w = ws_layout(T, desc);
     if (ws_bytes < w.total) return W4A4_ERR_SHAPE;
-    const uint8_t* b = (const uint8_t*)ws;
+    uint8_t* b = (uint8_t*)ws;
     return dev_status(launch_gemm(b + w.a_q, b + w.a_s, (const uint16_t*)(b + w.x_o), T, *desc, out, gelu,
+                                  (float*)(b + w.partial),
                                   (hipStream_t)stream));
 }
 
@@ -440,8 +442,9 @@ int w4a4_ffn_up_quantize(const void* X, int x_dtype, int64_t T, const w4a4_packe
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e = launch_ffn_prologue(*down, T, q, hs);
     if (e == hipSuccess) {
-        const uint8_t* u = b + w.up_base;
-        e = launch_gemm_quant(u + w.up.a_q, u + w.up.a_s, (const uint16_t*)(u + w.up.x_o), T, *up, q, hs);
+        uint8_t* u = b + w.up_base;
+        e = launch_gemm_quant(u + w.up.a_q, u + w.up.a_s, (const uint16_t*)(u + w.up.x_o), T, *up, q,
+                              (float*)(b + w.up_base + w.up.partial), hs);
     }
     return dev_status(e);
 }
@@ -458,12 +461,12 @@ int w4a4_ffn_forward(const void* X, int x_dtype, int64_t T, const w4a4_packed* u
     return gemm_into((uint8_t*)ws + w.down_base, w.down.total, T, down, Y, false, stream);
 }
 
-int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
+int w4a4_gemm_prequantized(void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc, float* Y,
                            void* stream) {
     return gemm_into(ws, ws_bytes, T, desc, Y, false, stream);
 }
 
-int w4a4_gemm_prequantized_gelu_bf16(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
+int w4a4_gemm_prequantized_gelu_bf16(void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
                                      uint16_t* H, void* stream) {
     return gemm_into(ws, ws_bytes, T, desc, H, true, stream);
 }
@@ -556,7 +559,8 @@ int w4a4_linear_dyn(const void* X, int x_dtype, int64_t T, const w4a4_packed_dyn
     d.W_O = W_O;
     e = launch_actprep(X, x_dtype, T, d, b + w.base.a_q, b + w.base.a_s, (uint16_t*)(b + w.base.x_o), hs);
     if (e == hipSuccess)
-        e = launch_gemm(b + w.base.a_q, b + w.base.a_s, (const uint16_t*)(b + w.base.x_o), T, d, Y, false, hs);
+        e = launch_gemm(b + w.base.a_q, b + w.base.a_s, (const uint16_t*)(b + w.base.x_o), T, d, Y, false,
+                        (float*)(b + w.base.partial), hs);
     return dev_status(e);
 }
 

@@ -103,18 +103,33 @@ __device__ __forceinline__ void tile_of(uint32_t bid, uint32_t nt_m, uint32_t nt
 // writes its A_q, A_s and X_O (QuantDst), bit-identical to the act-prep pass over H.
 constexpr int EPI_F32 = 0, EPI_GELU = 1, EPI_QUANT = 2;
 //
+// Split K for the last, partial round of tiles (the plan is gemm_split_plan): the
+// tiles [0, full) run whole; each remaining tile runs as `split` work items over
+// consecutive ranges of its K steps, each writing its fp32 accumulators to its own
+// 256 KiB block of `part` in register order.  A second launch (REDUCE) gives each
+// remaining tile one workgroup, which sums its blocks in range order and runs the
+// epilogue of the variant on the sum.
+struct SplitArgs {
+    float* part;
+    int64_t full;
+    int32_t split;
+};
+// Launch modes: whole tiles only (every split quantity a compile-time constant, so the
+// code is that of a kernel without the split), the split launch, and the reduce launch.
+constexpr int MODE_WHOLE = 0, MODE_SPLIT = 1, MODE_REDUCE = 2;
+//
 // Persistent: workgroup b walks the tiles b, b + G, b + 2G, ... of the grouped order
 // (G = grid size, one workgroup per CU; b and b + G sit on the same XCD), and its ring
 // of LDS slots runs on across tile boundaries: the last steps of one tile already
 // fetch the first steps of the next, whose operands are then in flight while this
 // tile's last MFMAs and its epilogue run.  The refill that the last step would issue
 // waits until the epilogue, which restages the accumulators through that free slot.
-template <int EPI>
+template <int EPI, int MODE>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As, const uint16_t* __restrict__ XO,
     int64_t T, const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs_rows,
     const uint16_t* __restrict__ WO, int64_t N, int64_t k_pad, int64_t k_ld, void* __restrict__ out,
-    int vec_store, QuantDst qd) {
+    int vec_store, QuantDst qd, SplitArgs sp) {
     float* __restrict__ Y = reinterpret_cast<float*>(out);
     uint16_t* __restrict__ H = reinterpret_cast<uint16_t*>(out);
     // the ring, then 1 KiB per wavefront that only the null loads of a tile's last
@@ -130,26 +145,47 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const int lh = lane >> 5;    // which 32-code half of a 64-code MFMA step this lane feeds
     const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
     const int64_t ntiles = nt_m * nt_n;
+    // work items: the whole tiles [0, sp.full), then sp.split K ranges of each later
+    // tile; the REDUCE launch has one item per later tile
+    const int64_t nitems = MODE == MODE_REDUCE  ? ntiles - sp.full
+                           : MODE == MODE_SPLIT ? sp.full + (ntiles - sp.full) * sp.split
+                                                : ntiles;
     int64_t id = blockIdx.x;
-    if (id >= ntiles) return;
+    if (id >= nitems) return;
 
     const int64_t o_ld = k_ld * 2;       // bytes per row of X_O / W_O
     const int nkb = (int)(k_pad / 128);  // FP4 steps (128 codes = 64 bytes per row)
     const int nbf = (int)(k_ld / 32);    // BF16 steps (32 values = 64 bytes per row)
     const int nsteps = nkb + nbf;
-    // Ring steps per tile: at least STAGES, so that the prefetch never reaches past the
-    // next tile; the extra steps read null descriptors (zeros) and add nothing.
-    const int ns = nsteps > STAGES ? nsteps : STAGES;
 
+    // A work item: a tile and the range [s0, s0 + len) of its K steps (steps are
+    // numbered FP4 first, then BF16).  Its ring steps ns are at least STAGES, so that the
+    // prefetch never reaches past the next item; the extra steps read null descriptors
+    // (zeros) and add nothing.  part: the partial-sum block of a K range, or -1.
     struct Tile {
-        int64_t t0, f0;
+        int64_t t0, f0, part;
+        int s0, len, ns;
         bool valid;
     };
     auto tile_at = [&](int64_t i) __attribute__((always_inline)) {
         Tile t;
-        t.valid = i < ntiles;
+        t.valid = i < nitems;
+        // 32-bit: the launcher keeps the item count below 2^31
+        uint32_t tile = (uint32_t)i;
+        t.part = -1;
+        t.s0 = 0;
+        t.len = nsteps;
+        if (MODE == MODE_SPLIT && i >= sp.full) {
+            const uint32_t q = (uint32_t)(i - sp.full), ns32 = (uint32_t)sp.split;
+            const uint32_t tq = q / ns32, c = q - tq * ns32;
+            tile = (uint32_t)sp.full + tq;
+            t.part = q;
+            t.s0 = (int)(c * (uint32_t)nsteps / ns32);
+            t.len = (int)((c + 1) * (uint32_t)nsteps / ns32) - t.s0;
+        }
+        t.ns = t.len > STAGES ? t.len : STAGES;
         uint32_t tm = 0, tn = 0;
-        if (t.valid) tile_of((uint32_t)i, (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
+        if (t.valid) tile_of(tile, (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
         t.t0 = (int64_t)tm * BT;
         t.f0 = (int64_t)tn * BF;
         return t;
@@ -203,9 +239,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             r[w] = __builtin_amdgcn_readfirstlane(c1 ? x[w] : (c2 ? y[w] : srd0[w]));
         return r;
     };
-    auto src_of = [&](const Tile& tl, int st) __attribute__((always_inline)) {
+    auto src_of = [&](const Tile& tl, int u) __attribute__((always_inline)) {   // u: the item's step
         Src r;
-        const bool fp4 = tl.valid && st < nkb, bf = tl.valid && !fp4 && st < nsteps;
+        const int st = tl.s0 + u;
+        const bool in = tl.valid && u < tl.len;
+        const bool fp4 = in && st < nkb, bf = in && !fp4;
         const int sts = fp4 ? st : 0;
         const int64_t ra = rows_a_of(tl), rb = rows_b_of(tl);
         r.fp4 = fp4;
@@ -218,25 +256,30 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         r.so = fp4 ? st * 1024 : (bf ? (st - nkb) * 64 : 0);
         return r;
     };
-    // The common case, an FP4 step of the current tile, with the per-tile parts
+    // The common case, an FP4 step of the current item, with the per-item parts
     // precomputed: only the scale descriptor's base and the code offset move per step
     // (rebuilding and selecting every descriptor each step would cost more scalar
-    // instructions than the scalar unit issues in a step's MFMA time).
+    // instructions than the scalar unit issues in a step's MFMA time).  The item's
+    // first step s0 is folded into the code descriptors (base + s0 KiB, range - s0 KiB:
+    // a row block b still passes the range check exactly when b is a valid block, since
+    // s0 < nkb and a lane offset within a block is below 1 KiB) and into the scale
+    // base, so the step offsets are the item's own.
     struct Fast {
         v4i a, b;
-        const uint8_t* sc;   // this wavefront's scale words of step 0
+        const uint8_t* sc;   // this wavefront's scale words of the item's first step
         uint32_t sc_bytes;
     };
     auto fast_of = [&](const Tile& tl) __attribute__((always_inline)) {
         Fast f;
         const int64_t ra = rows_a_of(tl), rb = rows_b_of(tl);
-        f.a = make_srd(Aq + (tl.t0 / 16) * blk, (uint32_t)((ra + 15) / 16 * blk));
-        f.b = make_srd(Bq + (tl.f0 / 16) * blk, (uint32_t)((rb + 15) / 16 * blk));
-        f.sc = sc_tbl + (sc_b ? tl.f0 : tl.t0) * 4;
+        const int64_t s0 = tl.s0 < nkb ? tl.s0 : nkb;   // items of BF16 steps only never use it
+        f.a = make_srd(Aq + (tl.t0 / 16) * blk + s0 * 1024, (uint32_t)((ra + 15) / 16 * blk - s0 * 1024));
+        f.b = make_srd(Bq + (tl.f0 / 16) * blk + s0 * 1024, (uint32_t)((rb + 15) / 16 * blk - s0 * 1024));
+        f.sc = sc_tbl + (s0 * sc_total + (sc_b ? tl.f0 : tl.t0)) * 4;
         f.sc_bytes = (uint32_t)((sc_b ? rb : ra) * 4);
         return f;
     };
-    auto fast_src = [&](const Fast& f, int st) __attribute__((always_inline)) {
+    auto fast_src = [&](const Fast& f, int st) __attribute__((always_inline)) {   // st: the item's step
         Src r;
         r.fp4 = 1;
         r.a = f.a;
@@ -425,9 +468,12 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         for (int i = 0; i < FF; ++i) {
             const int64_t fb = tl.f0 + wf * 64 + i * 32;   // the block's first feature (wave-uniform)
             if (fb >= N) continue;
-            const int64_t fl = fb + 4 * lh;                 // lane's features: fl + 8q + e
-            const bool has_j = fb < kj, all_j = fb + 32 <= kj;
-            const double* const rl = rs + (wf * 64 + i * 32 + 4 * lh);   // the lane's fl in the tile
+            // the lane's features are fb + o, o = 4 lh + 8q + e in [0, 32); the J
+            // positions among them are o < jl
+            const int64_t jlo = kj - fb;
+            const bool has_j = jlo > 0, all_j = jlo >= 32;
+            const int jl = has_j ? (all_j ? 32 : (int)jlo) : 0;
+            const double* const rl = rs + (wf * 64 + i * 32 + 4 * lh);   // the lane's first feature in the tile
 #pragma unroll
             for (int j = 0; j < FT; ++j) {
                 const int64_t t = tl.t0 + wt * 128 + j * 32 + l32;
@@ -450,7 +496,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                             const uint32_t w = hw[r / 2];
                             const float x = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
                             qv[r] = (float)((double)x * rr[e]);
-                            if (!all_j) qv[r] = fl + 8 * q + e < kj ? qv[r] : 0.0f;
+                            if (!all_j) qv[r] = 4 * lh + 8 * q + e < jl ? qv[r] : 0.0f;
                         }
                     }
                     float m4[4];
@@ -493,16 +539,70 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                     }
                 }
                 if (!all_j && tok) {
+                    // value r is feature fb + o, o = 4 lh + 8 (r / 4) + r % 4 in [0, 32); the
+                    // outlier slots are the o in [kj - fb, N - fb)
+                    const int64_t nhi = N - fb;
+                    const int o_min = jl, o_max = nhi > 32 ? 32 : (int)nhi;
+                    uint16_t* const xrow = qd.xo + t * qd.k_ld - jlo;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int64_t f = fl + 8 * (r / 4) + (r % 4);
-                        if (f >= kj && f < N)
-                            qd.xo[t * qd.k_ld + (f - kj)] = (uint16_t)((r & 1) ? (hw[r / 2] >> 16) : hw[r / 2]);
+                        const int o = 4 * lh + 8 * (r / 4) + (r % 4);
+                        if (o >= o_min && o < o_max)
+                            xrow[o] = (uint16_t)((r & 1) ? (hw[r / 2] >> 16) : hw[r / 2]);
                     }
                 }
             }
         }
     };
+
+    // A K range's accumulators, in register order: each store writes 1 KiB, 16 bytes
+    // per lane.  The REDUCE launch reads them back in the same order.
+    auto part_ptr = [&](int64_t blk_idx) __attribute__((always_inline)) {
+        return sp.part + blk_idx * (BT * BF) + wave * (FF * FT * 16 * 64) + lane * 4;
+    };
+    auto store_part = [&](const Tile& tl) __attribute__((always_inline)) {
+        float* p = part_ptr(tl.part);
+#pragma unroll
+        for (int i = 0; i < FF; ++i)
+#pragma unroll
+            for (int j = 0; j < FT; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f*>(p + ((i * FT + j) * 4 + q) * 256) =
+                        v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    };
+
+    if constexpr (MODE == MODE_REDUCE) {
+        // one later tile per workgroup: the sum of its K ranges' blocks, first to last,
+        // then the epilogue (ring slot 0 is free: nothing is in flight)
+        const int64_t q = id;
+        Tile tl;
+        uint32_t tm = 0, tn = 0;
+        tile_of((uint32_t)(sp.full + q), (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
+        tl.t0 = (int64_t)tm * BT;
+        tl.f0 = (int64_t)tn * BF;
+        tl.part = -1;
+        tl.s0 = 0;
+        tl.len = tl.ns = 0;
+        tl.valid = true;
+        for (int c = 0; c < sp.split; ++c) {
+            const float* p = part_ptr(q * sp.split + c);
+#pragma unroll
+            for (int i = 0; i < FF; ++i)
+#pragma unroll
+                for (int j = 0; j < FT; ++j)
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const v4f v = *reinterpret_cast<const v4f*>(p + ((i * FT + j) * 4 + qq) * 256);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][4 * qq + e] = c == 0 ? v[e] : acc[i][j][4 * qq + e] + v[e];
+                    }
+        }
+        if constexpr (EPI == EPI_QUANT) epilogue_quant(tl, 0);
+        else epilogue(tl, 0);
+        return;
+    }
 
     // Pipeline.  MFMAs issue in order, so the LDS fragment reads and the DMA issue
     // are interleaved one by one between the MFMAs of the other half-step, where
@@ -543,11 +643,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     zero_acc();
 
     constexpr int NM = FF * FT;   // MFMAs per half-step
-    int base = 0;                 // ring index of the current tile's step 0
+    int base = 0;                 // ring index of the current item's step 0
     for (;;) {
         const int64_t next_id = id + gridDim.x;
         const Tile nxt = tile_at(next_id);
         const Fast fc = fast_of(cur);
+        const int ns = cur.ns;
+        // the item's FP4 steps come first: [0, nfp4) of its own steps
+        const int nfp4 = cur.s0 >= nkb ? 0 : (nkb - cur.s0 < cur.len ? nkb - cur.s0 : cur.len);
         auto sync = [&]() __attribute__((always_inline)) {
             asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot st fully read
@@ -614,21 +717,22 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             half1(st, false, c1, c0, refill(st), st + 1 < ns);
         };
         int st = 0;
-        // steps whose refill is this tile's FP4 step st + STAGES
-        for (; st + 1 + STAGES < nkb; st += 2) {
+        // steps whose refill is this item's FP4 step st + STAGES
+        for (; st + 1 + STAGES < nfp4; st += 2) {
             fp4_step(st, c0, c1, true);
             fp4_step(st + 1, c1, c0, true);
         }
-        for (; st + 1 < nkb; st += 2) {
+        for (; st + 1 < nfp4; st += 2) {
             fp4_step(st, c0, c1, false);
             fp4_step(st + 1, c1, c0, false);
         }
-        if (st < nkb) fp4_step(st++, c0, c1, false);
+        if (st < nfp4) fp4_step(st++, c0, c1, false);
         for (; st < ns; ++st) bf16_step(st);
 
         // The last step's half 1 has already read the next tile's first fragments; they
         // are read again below so that no register holds them across the epilogue.
-        if constexpr (EPI == EPI_QUANT) epilogue_quant(cur, base + ns - 1);
+        if (MODE == MODE_SPLIT && cur.part >= 0) store_part(cur);
+        else if constexpr (EPI == EPI_QUANT) epilogue_quant(cur, base + ns - 1);
         else epilogue(cur, base + ns - 1);
         if (!nxt.valid) break;
         __syncthreads();   // every wavefront is done with the staging slot
@@ -656,39 +760,86 @@ static int64_t gemm_grid(int64_t tiles) {
     return tiles < g ? tiles : g;
 }
 
+// Split plan: the tiles that fill whole rounds of SPLIT_SLOTS workgroups (the CU count
+// of the part) run whole, and the remaining tail tiles (all tiles, when there are fewer
+// than SPLIT_SLOTS) are each cut into `split` K ranges, so that the last round keeps
+// most CUs busy.  A split is used only at 3 or more ranges per tile (at 2 the extra
+// partial-sum traffic and the reduce launch eat most of what the shorter round saves),
+// with at least SPLIT_MIN_STEPS K steps per range (a range pays about as much as a
+// dozen steps for its partial-sum store, its pipeline fill and its share of the reduce
+// launch).  Host logic only: the workspace size queries and the launch compute the same
+// plan.
+constexpr int64_t SPLIT_SLOTS = 256, SPLIT_MAX = 16, SPLIT_MIN = 3, SPLIT_MIN_STEPS = 16;
+
+GemmSplit gemm_split_plan(int64_t T, int64_t N, int64_t k_pad, int64_t k_ld) {
+    GemmSplit p;
+    const int64_t tiles = T > 0 && N > 0 ? ((T + BT - 1) / BT) * ((N + BF - 1) / BF) : 0;
+    p.full = tiles;
+    p.split = 1;
+    p.part_bytes = 0;
+    const int64_t tail = tiles < SPLIT_SLOTS ? tiles : tiles % SPLIT_SLOTS;
+    if (tail == 0) return p;
+    int64_t s = SPLIT_SLOTS / tail;
+    if (s > SPLIT_MAX) s = SPLIT_MAX;
+    const int64_t nsteps = k_pad / 128 + k_ld / 32;
+    if (s > nsteps / SPLIT_MIN_STEPS) s = nsteps / SPLIT_MIN_STEPS;
+    if (s < SPLIT_MIN) return p;
+    p.full = tiles - tail;
+    p.split = (int32_t)s;
+    p.part_bytes = (size_t)(tail * s) * BT * BF * sizeof(float);
+    return p;
+}
+
+namespace {
+
+template <int EPI>
+hipError_t launch_epi(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T, const w4a4_packed& d,
+                      void* out, int vec_store, const QuantDst& q, float* part, hipStream_t st) {
+    const int64_t tiles = ((T + BT - 1) / BT) * ((d.d_out + BF - 1) / BF);
+    const GemmSplit plan = gemm_split_plan(T, d.d_out, d.k_pad, d.k_ld);
+    if (plan.split > 1 && !part) return hipErrorInvalidValue;
+    const SplitArgs sp{part, plan.full, plan.split};
+    if (plan.split == 1) {
+        gemm_w4a4_kernel<EPI, MODE_WHOLE><<<dim3((unsigned)gemm_grid(tiles)), G_THREADS, 0, st>>>(
+            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+        return hipGetLastError();
+    }
+    const int64_t items = plan.full + (tiles - plan.full) * plan.split;
+    gemm_w4a4_kernel<EPI, MODE_SPLIT><<<dim3((unsigned)gemm_grid(items)), G_THREADS, 0, st>>>(
+        Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    gemm_w4a4_kernel<EPI, MODE_REDUCE><<<dim3((unsigned)(tiles - plan.full)), G_THREADS, 0, st>>>(
+        Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                       const w4a4_packed& d, void* out, bool gelu_bf16, hipStream_t st) {
+                       const w4a4_packed& d, void* out, bool gelu_bf16, float* part, hipStream_t st) {
     if (T <= 0 || d.d_out <= 0) return hipSuccess;
     const int64_t tiles = ((T + BT - 1) / BT) * ((d.d_out + BF - 1) / BF);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (tiles > 0x7FFFFFFF / SPLIT_MAX) return hipErrorInvalidValue;
     // 32-bit buffer offsets: one tile's rows of codes must span < 2 GiB
     if ((int64_t)BT * (d.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     // vector stores: 16 bytes (fp32) or 8 bytes (bf16) per lane, aligned when every row is
     const int vec_store = (d.d_out % 4 == 0) && (((uintptr_t)out & 15u) == 0);
-    const unsigned grid = (unsigned)gemm_grid(tiles);
     const QuantDst none{};
-    if (gelu_bf16)
-        gemm_w4a4_kernel<EPI_GELU><<<dim3(grid), G_THREADS, 0, st>>>(
-            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, none);
-    else
-        gemm_w4a4_kernel<EPI_F32><<<dim3(grid), G_THREADS, 0, st>>>(
-            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, none);
-    return hipGetLastError();
+    if (gelu_bf16) return launch_epi<EPI_GELU>(Aq, As, XO, T, d, out, vec_store, none, part, st);
+    return launch_epi<EPI_F32>(Aq, As, XO, T, d, out, vec_store, none, part, st);
 }
 
 hipError_t launch_gemm_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                             const w4a4_packed& up, const QuantDst& q, hipStream_t st) {
+                             const w4a4_packed& up, const QuantDst& q, float* part, hipStream_t st) {
     if (T <= 0 || up.d_out <= 0) return hipSuccess;
     const int64_t tiles = ((T + BT - 1) / BT) * ((up.d_out + BF - 1) / BF);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (tiles > 0x7FFFFFFF / SPLIT_MAX) return hipErrorInvalidValue;
     if ((int64_t)BT * (up.k_pad / 2) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     // the epilogue's 32-blocks are the down layer's: its K is the up layer's N, and its
     // k_j + k columns are the up layer's outputs
     if (q.k_j + q.k != up.d_out || q.k_pad % 128 != 0 || q.k_pad < q.k_j) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)gemm_grid(tiles);
-    gemm_w4a4_kernel<EPI_QUANT><<<dim3(grid), G_THREADS, 0, st>>>(
-        Aq, As, XO, T, up.B_q_tiles, up.B_s_rows, up.W_O, up.d_out, up.k_pad, up.k_ld, nullptr, 0, q);
-    return hipGetLastError();
+    return launch_epi<EPI_QUANT>(Aq, As, XO, T, up, nullptr, 0, q, part, st);
 }
 
 // rinv[p] = RN64(1 / s[J[p]]) for p < k_j (the reciprocal act-prep uses); zero codes

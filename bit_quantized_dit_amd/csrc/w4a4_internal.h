@@ -36,9 +36,19 @@ hipError_t launch_ffn_prologue(const w4a4_packed& down, int64_t T, const QuantDs
 // the epilogue: the up layer's output feature f is the down layer's compacted J
 // position f for f < k_j and its outlier slot f - k_j above.
 hipError_t launch_gemm_quant(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                             const w4a4_packed& up, const QuantDst& q, hipStream_t st);
+                             const w4a4_packed& up, const QuantDst& q, float* part, hipStream_t st);
 hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, int64_t T,
-                       const w4a4_packed& d, void* out, bool gelu_bf16, hipStream_t st);
+                       const w4a4_packed& d, void* out, bool gelu_bf16, float* part, hipStream_t st);
+// Split-K plan of the GEMM for T tokens and N outputs (host logic): tiles [0, full)
+// run whole, each later tile as `split` K ranges whose fp32 partial sums take
+// part_bytes of workspace (`part`, 256-byte aligned; unused and may be null when
+// split == 1).
+struct GemmSplit {
+    int64_t full;
+    int32_t split;
+    size_t part_bytes;
+};
+GemmSplit gemm_split_plan(int64_t T, int64_t N, int64_t k_pad, int64_t k_ld);
 
 hipError_t launch_gelu(const float* Y, int64_t n, uint16_t* H, hipStream_t st);
 

@@ -45,7 +45,7 @@ class W4A4Packed(ctypes.Structure):
 
 class W4A4WsLayout(ctypes.Structure):
     _fields_ = [("a_q", ctypes.c_size_t), ("a_s", ctypes.c_size_t), ("x_o", ctypes.c_size_t),
-                ("total", ctypes.c_size_t)]
+                ("partial", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class W4A4PackedDyn(ctypes.Structure):

@@ -129,6 +129,10 @@ typedef struct w4a4_ws_layout {
                          step-major: for each 128-code step the four codes of
                          token t sit at [(step*T + t)*4 .. +3]                 */
     size_t x_o;       /* bf16  [T][k_ld] outlier columns, zero padded         */
+    size_t partial;   /* fp32 partial sums of the GEMM's split-K tail tiles
+                         (scratch the GEMM writes and reads back within one
+                         call; empty when the tiles fill whole rounds of 256
+                         workgroups or too few would be split)              */
     size_t total;     /* bytes needed                                         */
 } w4a4_ws_layout;
 
@@ -186,8 +190,11 @@ int w4a4_quantize_activations(const void* X, int x_dtype, int64_t T, const w4a4_
 /* Dual-branch GEMM (sec. 3.3) on quantized activations already in `ws`:
  * Y[t][n] = sum_b 2^(Ea+Eb) sum_{p in b} a.b  (block-scaled FP4 MFMA)
  *         + sum_i X_O[t][i] W_O[n][i]         (BF16 MFMA, same fp32 accumulator)
- * Y device fp32 [T][d_out].  Async; never allocates. */
-int w4a4_gemm_prequantized(const void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
+ * Y device fp32 [T][d_out].  Reads A_q, A_s and X_O of `ws`; writes its `partial`
+ * region when the plan splits the last round of 256 x 256 output tiles along K
+ * (results then sum the K ranges' fp32 partials in a fixed order, so a given shape
+ * is bit-reproducible).  Async; never allocates. */
+int w4a4_gemm_prequantized(void* ws, size_t ws_bytes, int64_t T, const w4a4_packed* desc,
                            float* Y, void* stream);
 
 /* The per-call path: act-prep then the dual-branch GEMM.  Async; never allocates. */
@@ -298,7 +305,7 @@ int w4a4_search_alpha_k(const void* X_cal, int x_dtype, int64_t T_cal, int64_t d
  * H = bf16_rne(gelu_tanh(bf16_rne(y))) -- bit-identical to w4a4_gelu_tanh_bf16 over
  * the fp32 Y of the unfused call, without writing or re-reading Y.
  * H device bf16 [T][d_out] (16-byte aligned).  Async; never allocate. */
-int w4a4_gemm_prequantized_gelu_bf16(const void* ws, size_t ws_bytes, int64_t T,
+int w4a4_gemm_prequantized_gelu_bf16(void* ws, size_t ws_bytes, int64_t T,
                                      const w4a4_packed* desc, uint16_t* H, void* stream);
 int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc,
                           uint16_t* H, void* ws, size_t ws_bytes, void* stream);

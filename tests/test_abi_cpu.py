@@ -90,6 +90,42 @@ def test_workspace_layout_is_host_logic(L):
     assert L.w4a4_workspace_size(0, ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
 
 
+def test_split_plan_is_host_logic(L):
+    """The GEMM's split-K plan, seen through the workspace's partial-sum region (host
+    logic).  Tiles are 256 x 256; the tiles that fill whole rounds of 256 workgroups run
+    whole, the rest are cut into s = min(256 // tail, 16, K steps // 16) ranges of K when
+    s >= 3, each range taking a 256 KiB block of fp32 partial sums."""
+    out = B.W4A4WsLayout()
+    blk = 256 * 256 * 4
+
+    def partial(T, d_in, d_out, k):
+        d = _fake_desc(d_in, d_out, k)
+        assert L.w4a4_workspace_layout(T, ctypes.byref(d), ctypes.byref(out)) == 0
+        assert out.partial >= out.x_o and out.total % 256 == 0
+        return out.total - out.partial
+
+    # 4096 tokens, 13824 -> 5120: 16 x 20 = 320 tiles, 64 in the last round, 110 K steps
+    assert partial(4096, 13824, 5120, 64) == 64 * 4 * blk
+    # 57600 tokens, 5120 -> 13824: 225 x 54 tiles, a tail of 118 would give 2 ranges: whole
+    assert partial(57600, 5120, 13824, 128) == 0
+    # 4096 tokens, 5120 -> 13824: 864 tiles, a tail of 96: 2 ranges, whole
+    assert partial(4096, 5120, 13824, 64) == 0
+    # 7200 tokens, 13824 -> 5120: 29 x 20 = 580 tiles, a tail of 68: 3 ranges
+    assert partial(7200, 13824, 5120, 64) == 68 * 3 * blk
+    # 256 tokens, 5120 -> 13824: 54 tiles, but 43 K steps allow only 2 ranges: whole
+    assert partial(256, 5120, 13824, 128) == 0
+    # 256 tokens, 13824 -> 5120: 20 tiles, 110 K steps: 6 ranges (12 tiles' worth allowed)
+    assert partial(256, 13824, 5120, 64) == 20 * 6 * blk
+    # one tile, 20000 inputs (158 K steps): 9 ranges
+    assert partial(40, 20000, 64, 16) == 9 * blk
+    # one tile, 32768 inputs half of them outliers (128 FP4 + 512 BF16 steps): the
+    # 16-range cap
+    assert partial(16, 32768, 64, 16384) == 16 * blk
+    # short K (5 steps): never split; a round of exactly 256 tiles: nothing left over
+    assert partial(1000, 512, 1024, 16) == 0
+    assert partial(256 * 16, 5120, 256 * 16, 64) == 0
+
+
 def test_dynamic_sizes_are_host_logic(L):
     """Per-call outlier selection: blob and workspace sizes, and the shape rules (d_in
     even and at most 16384 so one workgroup sorts every column's score)."""

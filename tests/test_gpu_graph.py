@@ -38,18 +38,19 @@ def _capture_and_check(call, Y, Y_eager, between):
     _banner(f"  {REPLAYS} replays bit-identical to the eager call")
 
 
-def _small_layer(layout):
+def _small_layer(T=300, d_in=704, d_out=320, k=13):
     spec = synth.WORKLOADS[2]
-    inp = synth.layer_inputs(spec, T=300, d_in=704, d_out=320, k=13, T_cal=96)
+    inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=96)
     X, Xc, W = to_dev(inp["X"]), to_dev(inp["X_cal"]), to_dev(inp["W"])
-    s, O, _, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, 13)
+    s, O, _, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, k)
     return X, W, s, O
 
 
-@pytest.mark.parametrize("layout", [0, 1])
-def test_linear_graph_replays(layout):
-    _banner(f"graph capture: w4a4_linear T=300 704->320 k=13 layout {layout}")
-    X, W, s, O = _small_layer(layout)
+@pytest.mark.parametrize("layout,T,d_in,d_out,k", [(0, 300, 704, 320, 13), (1, 300, 704, 320, 13),
+                                                   (0, 200, 8192, 600, 20)])   # split K: two launches
+def test_linear_graph_replays(layout, T, d_in, d_out, k):
+    _banner(f"graph capture: w4a4_linear T={T} {d_in}->{d_out} k={k} layout {layout}")
+    X, W, s, O = _small_layer(T, d_in, d_out, k)
     packed = B.w4a4_pack_weights(W, s, O, layout)
     T, N = X.shape[0], W.shape[0]
     ws, ws2 = B.alloc_workspace(T, packed), B.alloc_workspace(T, packed)
@@ -62,7 +63,7 @@ def test_linear_graph_replays(layout):
 
 def test_linear_dyn_graph_replays():
     _banner("graph capture: w4a4_linear_dyn T=300 704->320 k=13")
-    X, W, s, _ = _small_layer(0)
+    X, W, s, _ = _small_layer()
     pk = B.w4a4_pack_weights_dyn(W, s, 13, 0)
     T, N = X.shape[0], W.shape[0]
     ws = B.alloc_workspace_dyn(T, pk)

@@ -28,6 +28,11 @@ SMALL = [
     (77, 333, 96, 5, 0, "f32"),         # odd d_in: the generic act-prep kernel
     (45, 333, 70, 7, 1, "bf16"),        # odd d_in, bf16 rows at odd element offsets
     (40, 20000, 64, 16, 0, "bf16"),     # d_in beyond the fast act-prep paths (16384)
+    # split K (fewer tiles than CUs): each tile runs as several K ranges whose partial
+    # sums a second launch adds up
+    (70, 4608, 300, 512, 0, "bf16"),    # 3 ranges of 16 steps: the last is all BF16 steps
+    (600, 6400, 520, 24, 2, "f32"),     # 9 ragged tiles x 3 ranges
+    (64, 7168, 256, 128, 0, "bf16"),    # the last range mixes FP4 and BF16 steps
 ]
 
 
@@ -187,7 +192,8 @@ def test_e2m1_threshold_neighbourhoods(orc):
     _banner(f"  {X.size} elements in {T} rows")
 
 
-@pytest.mark.parametrize("T,d_in,d_out,k,layout,dt", [(300, 700, 203, 13, 0, "f32"), (520, 1000, 512, 40, 2, "bf16")])
+@pytest.mark.parametrize("T,d_in,d_out,k,layout,dt", [(300, 700, 203, 13, 0, "f32"), (520, 1000, 512, 40, 2, "bf16"),
+                                                     (200, 8192, 300, 20, 0, "bf16")])   # split K
 def test_fused_gelu_matches_unfused(orc, T, d_in, d_out, k, layout, dt):
     """w4a4_linear_gelu_bf16 writes exactly w4a4_gelu_tanh_bf16(w4a4_linear(X)), on a
     ragged tile grid and (203 outputs) the unvectorised store path."""
@@ -304,6 +310,8 @@ FFN_FUSED = [
     (257, 384, 640, 4, 128, 2, 1, "bf16", False),  # k_j = 512 = k_pad: no pad
     (70, 256, 700, 6, 12, 0, 0, "bf16", False),    # d_ff = 700: the block at 672 holds J, O and
                                                    # columns past d_ff
+    (100, 6144, 512, 8, 16, 0, 2, "bf16", False),  # the up GEMM split along K (3 ranges)
+    (64, 256, 8192, 4, 16, 0, 0, "bf16", False),   # the down GEMM split along K (4 ranges)
 ]
 
 
@@ -405,6 +413,39 @@ def test_determinism_and_prequantized_split(orc):
     B.w4a4_linear(Xd, r["packed"], Y3, ws2)
     torch.cuda.synchronize()
     assert torch.equal(r["Y"].view(torch.int32), Y3.view(torch.int32))
+
+
+SPLIT = [
+    # T, d_in, d_out, k, layout: shapes whose GEMM the plan splits along K
+    (64, 7168, 256, 128, 0),     # 1 tile x 3 ranges; the last mixes FP4 and BF16 steps
+    (70, 4608, 300, 512, 0),     # the last range is BF16 steps only
+    (600, 6400, 520, 24, 2),     # 9 ragged tiles x 3 ranges
+    (40, 20000, 64, 16, 0),      # 9 ranges
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,layout", SPLIT)
+def test_split_k_is_planned_and_deterministic(T, d_in, d_out, k, layout):
+    """These shapes take the split-K path (a partial-sum region in the workspace), and
+    their results are bitwise reproducible: the partial sums are added in a fixed order
+    (the oracle comparison of the same shapes is in test_layer_parity)."""
+    _banner(f"split K T={T} d_in={d_in} d_out={d_out} k={k}")
+    spec = synth.WORKLOADS[2]
+    inp = synth.layer_inputs(spec, T=T, d_in=d_in, d_out=d_out, k=k, T_cal=64)
+    X, Xc, W = to_dev(inp["X"]), to_dev(inp["X_cal"]), to_dev(inp["W"])
+    s, O, _, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, k)
+    packed = B.w4a4_pack_weights(W, s, O, layout)
+    L = B.w4a4_workspace_layout(T, packed)
+    assert L.total - L.partial >= 256 * 256 * 4 * 3, "the plan does not split this shape"
+    ws = B.alloc_workspace(T, packed)
+    ws.fill_(0x7F)                      # stale partial sums must not leak into Y
+    Y1 = torch.empty(T, d_out, device="cuda")
+    B.w4a4_linear(X, packed, Y1, ws)
+    Y2 = torch.full((T, d_out), float("nan"), device="cuda")
+    B.w4a4_linear(X, packed, Y2, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y1).all())
+    assert bool(torch.equal(Y1.view(torch.int32), Y2.view(torch.int32)))
 
 
 def test_error_paths_on_device():
