@@ -33,6 +33,7 @@ SMALL = [
     (70, 4608, 300, 512, 0, "bf16"),    # 3 ranges of 16 steps: the last is all BF16 steps
     (600, 6400, 520, 24, 2, "f32"),     # 9 ragged tiles x 3 ranges
     (64, 7168, 256, 128, 0, "bf16"),    # the last range mixes FP4 and BF16 steps
+    (1, 8192, 100, 16, 1, "bf16"),      # one token, ragged outputs, 32x32 tiles, 4 ranges
 ]
 
 
