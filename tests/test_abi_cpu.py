@@ -126,6 +126,36 @@ def test_split_plan_is_host_logic(L):
     assert partial(256 * 16, 5120, 256 * 16, 64) == 0
 
 
+def test_split_plan_invariants(L):
+    """Over random shapes: the partial-sum region is whole 256 KiB blocks, one per K
+    range of a tail tile; ranges hold at least 16 K steps; at most 255 tail tiles x 16
+    ranges; every split puts at least 3 ranges on each tail tile and no more items in
+    the last round than there are workgroup slots (256)."""
+    rng = np.random.default_rng(7)
+    out = B.W4A4WsLayout()
+    blk = 256 * 256 * 4
+    for _ in range(400):
+        T = int(rng.integers(1, 70000))
+        d_in = int(rng.integers(2, 32769))
+        d_out = int(rng.integers(1, 20000))
+        k = int(rng.integers(0, min(d_in, 512) + 1))
+        d = _fake_desc(d_in, d_out, k)
+        assert L.w4a4_workspace_layout(T, ctypes.byref(d), ctypes.byref(out)) == 0
+        nbytes = out.total - out.partial
+        # the region is padded to 256 bytes; blocks are 256 KiB, so it is exact
+        assert nbytes % blk == 0
+        blocks = nbytes // blk
+        tiles = -(-T // 256) * -(-d_out // 256)
+        tail = tiles if tiles < 256 else tiles % 256
+        nsteps = d.k_pad // 128 + d.k_ld // 32
+        if blocks:
+            assert tail > 0 and blocks % tail == 0
+            s = blocks // tail
+            assert 3 <= s <= 16 and nsteps // s >= 16 and tail * s <= 256
+        else:
+            assert tail == 0 or min(256 // tail, 16, nsteps // 16) < 3
+
+
 def test_dynamic_sizes_are_host_logic(L):
     """Per-call outlier selection: blob and workspace sizes, and the shape rules (d_in
     even and at most 16384 so one workgroup sorts every column's score)."""
