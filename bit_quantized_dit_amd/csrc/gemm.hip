@@ -107,8 +107,9 @@ constexpr int EPI_F32 = 0, EPI_GELU = 1, EPI_QUANT = 2;
 // tiles [0, full) run whole; each remaining tile runs as `split` work items over
 // consecutive ranges of its K steps, each writing its fp32 accumulators to its own
 // 256 KiB block of `part` in register order.  A second launch (REDUCE) gives each
-// remaining tile one workgroup, which sums its blocks in range order and runs the
-// epilogue of the variant on the sum.
+// wavefront sub-tile of each remaining tile a one-wavefront workgroup, which sums that
+// sub-tile's parts of the blocks in range order and runs the variant's epilogue on the
+// sum (eight workgroups per tile, so the partial sums stream through many CUs).
 struct SplitArgs {
     float* part;
     int64_t full;
@@ -134,11 +135,15 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     uint16_t* __restrict__ H = reinterpret_cast<uint16_t*>(out);
     // the ring, then 1 KiB per wavefront that only the null loads of a tile's last
     // step write (never read)
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * SLOT_BYTES + (G_THREADS / 64) * 1024];
+    // the reduce launch stages its epilogue through one slot and fetches nothing
+    constexpr int SMEM_BYTES = MODE == MODE_REDUCE ? SLOT_BYTES : STAGES * SLOT_BYTES + (G_THREADS / 64) * 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    // wave-uniform (SGPR); a reduce workgroup is one wavefront standing in for wavefront
+    // blockIdx % 8 of its tile
+    const int wave = MODE == MODE_REDUCE ? (int)(blockIdx.x & 7) : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wt = wave & 1;     // token half of the tile
     const int wf = wave >> 1;    // feature quarter of the tile
     const int l32 = lane & 31;
@@ -146,8 +151,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
     const int64_t ntiles = nt_m * nt_n;
     // work items: the whole tiles [0, sp.full), then sp.split K ranges of each later
-    // tile; the REDUCE launch has one item per later tile
-    const int64_t nitems = MODE == MODE_REDUCE  ? ntiles - sp.full
+    // tile; the REDUCE launch has one item per wavefront sub-tile of each later tile
+    const int64_t nitems = MODE == MODE_REDUCE  ? (ntiles - sp.full) * (G_THREADS / 64)
                            : MODE == MODE_SPLIT ? sp.full + (ntiles - sp.full) * sp.split
                                                 : ntiles;
     int64_t id = blockIdx.x;
@@ -459,7 +464,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         const uint32_t sel_lo = lh ? 0x05040100u : 0x01000504u;
         const uint32_t sel_hi = lh ? 0x07060302u : 0x03020706u;
         double* const rs = reinterpret_cast<double*>(smem + (g & (STAGES - 1)) * SLOT_BYTES);
-        if (tid < BF) {
+        if constexpr (MODE == MODE_REDUCE) {   // one wavefront: its own 64 features
+            const int r = wf * 64 + lane;
+            const int64_t f = tl.f0 + r;
+            rs[r] = f < kj ? qd.rinv[f] : 0.0;
+        } else if (tid < BF) {
             const int64_t f = tl.f0 + tid;
             rs[tid] = f < kj ? qd.rinv[f] : 0.0;
         }
@@ -573,9 +582,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     };
 
     if constexpr (MODE == MODE_REDUCE) {
-        // one later tile per workgroup: the sum of its K ranges' blocks, first to last,
-        // then the epilogue (ring slot 0 is free: nothing is in flight)
-        const int64_t q = id;
+        // one wavefront's sub-tile of a later tile per workgroup (one wavefront): the sum
+        // of its K ranges' blocks, first to last, then that wavefront's part of the
+        // epilogue, staged through slot 0 (the epilogues are per wavefront)
+        const int64_t q = id / (G_THREADS / 64);
         Tile tl;
         uint32_t tm = 0, tn = 0;
         tile_of((uint32_t)(sp.full + q), (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
@@ -809,7 +819,7 @@ hipError_t launch_epi(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, 
         Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    gemm_w4a4_kernel<EPI, MODE_REDUCE><<<dim3((unsigned)(tiles - plan.full)), G_THREADS, 0, st>>>(
+    gemm_w4a4_kernel<EPI, MODE_REDUCE><<<dim3((unsigned)((tiles - plan.full) * (G_THREADS / 64))), 64, 0, st>>>(
         Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
     return hipGetLastError();
 }
