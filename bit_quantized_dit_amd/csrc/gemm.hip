@@ -61,7 +61,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int G_THREADS = 512;               // 8 wavefronts: 2 per SIMD
 constexpr int BT = 256;                      // tokens per workgroup tile
-constexpr int BF = 256;                      // features per workgroup tile
+constexpr int BF = 256;                      // features per workgroup tile (the tile grid's width)
 constexpr int FT = 4;                        // 32-token MFMA tiles per wavefront (128 tokens)
 constexpr int FF = 2;                        // 32-feature MFMA tiles per wavefront (64 features)
 constexpr int ROW_BYTES = 64;                // 128 FP4 codes per row per K step
@@ -116,8 +116,11 @@ struct SplitArgs {
     int32_t split;
 };
 // Launch modes: whole tiles only (every split quantity a compile-time constant, so the
-// code is that of a kernel without the split), the split launch, and the reduce launch.
-constexpr int MODE_WHOLE = 0, MODE_SPLIT = 1, MODE_REDUCE = 2;
+// code is that of a kernel without the split), the split launch, the reduce launch,
+// and half tiles: the tail tiles [full, ntiles) of the 256 x 256 grid each run as two
+// 256-token x 128-feature items, with four wavefronts along the tokens (64 each) and
+// two along the features, one B row block per wavefront, and four loads per step.
+constexpr int MODE_WHOLE = 0, MODE_SPLIT = 1, MODE_REDUCE = 2, MODE_HALF = 3;
 //
 // Persistent: workgroup b walks the tiles b, b + G, b + 2G, ... of the grouped order
 // (G = grid size, one workgroup per CU; b and b + G sit on the same XCD), and its ring
@@ -139,22 +142,35 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     constexpr int SMEM_BYTES = MODE == MODE_REDUCE ? SLOT_BYTES : STAGES * SLOT_BYTES + (G_THREADS / 64) * 1024;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
 
+    // this instance's tile: BF features (the grid stays 256 wide: ::w4a4::BF), FT
+    // 32-token MFMA tiles per wavefront, WT wavefronts along the tokens, NB B row blocks
+    // of 16 rows per wavefront per step, DPS loads per wavefront per step
+    constexpr int BF = MODE == MODE_HALF ? 128 : ::w4a4::BF;
+    constexpr int FT = BF == 256 ? 4 : 2;
+    constexpr int WT = BT / (FT * 32);
+    constexpr int NB = BF / 128;
+    constexpr int DPS = 2 + NB + 1;
+    constexpr int AS_OFF = (BT + BF) * ROW_BYTES;
+    constexpr int BS_OFF = AS_OFF + BT * 4;
+    static_assert(BS_OFF + BF * 4 <= SLOT_BYTES && WT * (BF / 64) == G_THREADS / 64, "tile geometry");
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform (SGPR); a reduce workgroup is one wavefront standing in for wavefront
     // blockIdx % 8 of its tile
     const int wave = MODE == MODE_REDUCE ? (int)(blockIdx.x & 7) : __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wt = wave & 1;     // token half of the tile
-    const int wf = wave >> 1;    // feature quarter of the tile
+    const int wt = wave % WT;    // which FT * 32 tokens of the tile
+    const int wf = wave / WT;    // which 64 features of the tile
     const int l32 = lane & 31;
     const int lh = lane >> 5;    // which 32-code half of a 64-code MFMA step this lane feeds
-    const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + BF - 1) / BF;
+    const int64_t nt_m = (T + BT - 1) / BT, nt_n = (N + ::w4a4::BF - 1) / ::w4a4::BF;
     const int64_t ntiles = nt_m * nt_n;
     // work items: the whole tiles [0, sp.full), then sp.split K ranges of each later
     // tile; the REDUCE launch has one item per wavefront sub-tile of each later tile
     const int64_t nitems = MODE == MODE_REDUCE  ? (ntiles - sp.full) * (G_THREADS / 64)
                            : MODE == MODE_SPLIT ? sp.full + (ntiles - sp.full) * sp.split
-                                                : ntiles;
+                           : MODE == MODE_HALF  ? (ntiles - sp.full) * 2
+                                                : sp.full;
     int64_t id = blockIdx.x;
     if (id >= nitems) return;
 
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         Tile t;
         t.valid = i < nitems;
         // 32-bit: the launcher keeps the item count below 2^31
-        uint32_t tile = (uint32_t)i;
+        uint32_t tile = MODE == MODE_HALF ? (uint32_t)(sp.full + (i >> 1)) : (uint32_t)i;
         t.part = -1;
         t.s0 = 0;
         t.len = nsteps;
@@ -192,11 +208,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         uint32_t tm = 0, tn = 0;
         if (t.valid) tile_of(tile, (uint32_t)nt_m, (uint32_t)nt_n, tm, tn);
         t.t0 = (int64_t)tm * BT;
-        t.f0 = (int64_t)tn * BF;
+        t.f0 = (int64_t)tn * ::w4a4::BF + (MODE == MODE_HALF ? (i & 1) * BF : 0);
         return t;
     };
     auto rows_a_of = [&](const Tile& t) __attribute__((always_inline)) { return T - t.t0 < BT ? T - t.t0 : (int64_t)BT; };
-    auto rows_b_of = [&](const Tile& t) __attribute__((always_inline)) { return N - t.f0 < BF ? N - t.f0 : (int64_t)BF; };
+    // (the second half of a ragged last column of tiles may lie past N: no rows)
+    auto rows_b_of = [&](const Tile& t) __attribute__((always_inline)) {
+        return N - t.f0 < BF ? (N > t.f0 ? N - t.f0 : (int64_t)0) : (int64_t)BF;
+    };
 
     // FP4 codes in the tiled order (1 KiB per 16-row block and step, the LDS swizzle
     // already applied): a tile's 16 row blocks start blk bytes apart.  Step-major
@@ -212,16 +231,23 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // for the FP4 codes (lane -> 16 contiguous bytes); the row-major bf16 outlier
     // operands are gathered into the same order: lane -> row 16b + lane/4, physical
     // chunk lane%4, logical chunk = physical ^ ((row >> 2) & 3)
-    int voff[2], voffo[2];
+    // (A: blocks 2w, 2w+1; B: the same, or block w when a wavefront has one B block)
+    int voff[2], voffo[2], vb[2], vbo[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int row = 16 * (wave * 2 + h) + (lane >> 2);
         const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
         voff[h] = (wave * 2 + h) * (int)blk + lane * 16;
         voffo[h] = row * (int)o_ld + chunk;
+        const int bb = NB == 2 ? wave * 2 + h : wave;
+        const int rowb = 16 * bb + (lane >> 2);
+        vb[h] = bb * (int)blk + lane * 16;
+        vbo[h] = rowb * (int)o_ld + (((lane & 3) ^ ((rowb >> 2) & 3)) << 4);
     }
-    // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words
+    // waves 0-3 copy the A scale words of rows 64w.., waves 4-7 the B scale words (in a
+    // half tile waves 6 and 7 have no B rows: their scale loads go to the spare KiB)
     const bool sc_b = wave >= 4;
+    const bool sc_live = !sc_b || (wave & 3) * 64 < BF;
     const int vsc = (64 * (wave & 3) + lane) * 4;
     const uint8_t* const sc_tbl = sc_b ? Bs_rows : As;   // this wavefront's step-major scale array
     const int64_t sc_total = sc_b ? N : T;               // its rows per step
@@ -229,7 +255,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // Step st of tile tl: FP4 codes + scales for st < nkb, the 64-byte column slice
     // (st - nkb) of X_O / W_O for BF16 steps, and a null descriptor past the tile's
     // steps or for no tile (zero range: the loads return zeros and touch no memory).
-    // Every step issues exactly DMA_PER_STAGE loads per wavefront, so the outstanding
+    // Every step issues exactly DPS loads per wavefront, so the outstanding
     // count, and with it every wait below, is the same on every step.
     struct Src {
         v4i a, b, sc;   // A and B operands, this wavefront's scale words
@@ -299,19 +325,20 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // live = false sends the (null) load to this wavefront's scratch KiB instead
     const uint32_t spare = lds0 + STAGES * SLOT_BYTES + wave * 1024;
     auto dma_code = [&](const Src& r, uint32_t slot, int h, int which, bool live = true) __attribute__((always_inline)) {
-        const int vo = r.fp4 ? voff[h] : voffo[h];
-        const uint32_t dst = slot + (which == 0 ? A_OFF : B_OFF) + (wave * 2 + h) * 1024;
+        const int vo = which == 0 ? (r.fp4 ? voff[h] : voffo[h]) : (r.fp4 ? vb[h] : vbo[h]);
+        const uint32_t dst = slot + (which == 0 ? A_OFF + (wave * 2 + h) * 1024
+                                                : B_OFF + (NB == 2 ? wave * 2 + h : wave) * 1024);
         dma16(which == 0 ? r.a : r.b, live ? dst : spare, vo, r.so);
     };
     auto dma_scale = [&](const Src& r, uint32_t slot, bool live = true) __attribute__((always_inline)) {
         const uint32_t dst = slot + (sc_b ? BS_OFF : AS_OFF) + (wave & 3) * 256;
-        dma4(r.sc, live ? dst : spare, vsc, 0);
+        dma4(r.sc, live && sc_live ? dst : spare, vsc, 0);
     };
     auto issue = [&](const Src& r, uint32_t slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) dma_code(r, slot, h, 1);
+        for (int h = 0; h < NB; ++h) dma_code(r, slot, h, 1);
         dma_scale(r, slot);
     };
 
@@ -332,14 +359,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     };
     auto load_a = [&](Frags& f, int g, int h, int j) __attribute__((always_inline)) {
         const uint8_t* slot = smem + (g & (STAGES - 1)) * SLOT_BYTES;
-        const int r = wt * 128 + j * 32 + l32;
+        const int r = wt * (FT * 32) + j * 32 + l32;
         const uint4 q = *reinterpret_cast<const uint4*>(slot + A_OFF + swz(r, 2 * h + lh));
         f.a[j] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
     };
     auto load_scale = [&](Scales& c, int g, int o) __attribute__((always_inline)) {   // o-th of 6 words
         const uint8_t* slot = smem + (g & (STAGES - 1)) * SLOT_BYTES;
         if (o < FF) c.b[o] = reinterpret_cast<const uint32_t*>(slot + BS_OFF)[wf * 64 + o * 32 + l32];
-        else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * 128 + (o - FF) * 32 + l32];
+        else c.a[o - FF] = reinterpret_cast<const uint32_t*>(slot + AS_OFF)[wt * (FT * 32) + (o - FF) * 32 + l32];
     };
     // A row's scale word holds the E8M0 bytes of its four 32-blocks of the step, and lane
     // l feeds block 2h + l/32 in half-step h.  Each word is shifted right by 8 * (l / 32)
@@ -407,7 +434,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                 for (int k = 0; k < 4; ++k) {
                     const int r = (lane >> 4) + 4 * k;
                     const v4f v = *reinterpret_cast<const v4f*>(stage + r * SROW + (lane & 15) * 4);
-                    const int64_t t = tl.t0 + wt * 128 + j * 32 + hh * 16 + r;
+                    const int64_t t = tl.t0 + wt * (FT * 32) + j * 32 + hh * 16 + r;
                     const int64_t n = tl.f0 + wf * 64 + (lane & 15) * 4;
                     if constexpr (EPI == EPI_GELU) {
                         const uint32_t h01 = gelu_tanh_bf16x2(v[0], v[1]), h23 = gelu_tanh_bf16x2(v[2], v[3]);
@@ -485,7 +512,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             const double* const rl = rs + (wf * 64 + i * 32 + 4 * lh);   // the lane's first feature in the tile
 #pragma unroll
             for (int j = 0; j < FT; ++j) {
-                const int64_t t = tl.t0 + wt * 128 + j * 32 + l32;
+                const int64_t t = tl.t0 + wt * (FT * 32) + j * 32 + l32;
                 const bool tok = t < T;
                 uint32_t hw[8];
 #pragma unroll
@@ -633,11 +660,12 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // loads of the last step, the epilogue's stores, the deferred refill), which only
     // makes those two waits stricter.  The FP4 steps run first, then the BF16 steps
     // of the outlier branch on the same ring.
-    static_assert(STAGES == 4 && DMA_PER_STAGE == 5, "vmcnt immediates below assume 4 x 5");
+    static_assert(STAGES == 4 && (DPS == 5 || DPS == 4), "vmcnt immediates below assume 4 x 5 or 4 x 4");
     Tile cur = tile_at(id);
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) issue(src_of(cur, st), slot_of(st));
-    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    if constexpr (DPS == 5) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     __syncthreads();
     Frags f0, f1;
     Scales c0, c1;                 // scale words of the current and of the next step
@@ -662,7 +690,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
         // the item's FP4 steps come first: [0, nfp4) of its own steps
         const int nfp4 = cur.s0 >= nkb ? 0 : (nkb - cur.s0 < cur.len ? nkb - cur.s0 : cur.len);
         auto sync = [&]() __attribute__((always_inline)) {
-            asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            if constexpr (DPS == 5) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot st fully read
             __syncthreads();
         };
@@ -688,9 +717,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                     load_half(f0, base + st + 1, 0, s);
                     load_scale(nx, base + st + 1, s);
                 }
-                if (s == 1 || s == 2) dma_code(r, slot, s - 1, 0, dma);
-                if (s == 3 || s == 4) dma_code(r, slot, s - 3, 1, dma);
-                if (s == 5) dma_scale(r, slot, dma);
+                // the step's loads spread over the MFMAs: A blocks, B blocks, scales
+                constexpr int D0 = NM >= 6 ? 1 : 0;
+                if (s == D0 || s == D0 + 1) dma_code(r, slot, s - D0, 0, dma);
+                if (s >= D0 + 2 && s < D0 + 2 + NB) dma_code(r, slot, s - D0 - 2, 1, dma);
+                if (s == D0 + 2 + NB) dma_scale(r, slot, dma);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -773,7 +804,12 @@ static int64_t gemm_grid(int64_t tiles) {
 // Split plan: the tiles that fill whole rounds of SPLIT_SLOTS workgroups (the CU count
 // of the part) run whole, and the remaining tail tiles (all tiles, when there are fewer
 // than SPLIT_SLOTS) are each cut into `split` K ranges, so that the last round keeps
-// most CUs busy.  A split is used only at 3 or more ranges per tile (at 2 the extra
+// most CUs busy.  A layer whose tiles are not split and all fit twice into the slots
+// (at most 128 tiles) runs as half tiles (256 x 128): one round of half the length,
+// with no partial sums.  (Half tiles for the tail after whole rounds were measured
+// slower: the second launch's gap and the half tile's larger DMA share per FLOP
+// outweigh the shorter last round: 57600 x 5120 -> 13824, 2297-2299 against 2282-2285
+// us.)  A split is used only at 3 or more ranges per tile (at 2 the extra
 // partial-sum traffic and the reduce launch eat most of what the shorter round saves),
 // with at least SPLIT_MIN_STEPS K steps per range (a range pays about as much as a
 // dozen steps for its partial-sum store, its pipeline fill and its share of the reduce
@@ -787,13 +823,20 @@ GemmSplit gemm_split_plan(int64_t T, int64_t N, int64_t k_pad, int64_t k_ld) {
     p.full = tiles;
     p.split = 1;
     p.part_bytes = 0;
+    p.half = 0;
     const int64_t tail = tiles < SPLIT_SLOTS ? tiles : tiles % SPLIT_SLOTS;
     if (tail == 0) return p;
     int64_t s = SPLIT_SLOTS / tail;
     if (s > SPLIT_MAX) s = SPLIT_MAX;
     const int64_t nsteps = k_pad / 128 + k_ld / 32;
     if (s > nsteps / SPLIT_MIN_STEPS) s = nsteps / SPLIT_MIN_STEPS;
-    if (s < SPLIT_MIN) return p;
+    if (s < SPLIT_MIN) {
+        if (2 * tail <= SPLIT_SLOTS && tail == tiles) {
+            p.full = tiles - tail;
+            p.half = 1;
+        }
+        return p;
+    }
     p.full = tiles - tail;
     p.split = (int32_t)s;
     p.part_bytes = (size_t)(tail * s) * BT * BF * sizeof(float);
@@ -810,8 +853,15 @@ hipError_t launch_epi(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO, 
     if (plan.split > 1 && !part) return hipErrorInvalidValue;
     const SplitArgs sp{part, plan.full, plan.split};
     if (plan.split == 1) {
-        gemm_w4a4_kernel<EPI, MODE_WHOLE><<<dim3((unsigned)gemm_grid(tiles)), G_THREADS, 0, st>>>(
-            Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+        if (plan.full > 0)
+            gemm_w4a4_kernel<EPI, MODE_WHOLE><<<dim3((unsigned)gemm_grid(plan.full)), G_THREADS, 0, st>>>(
+                Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+        if (plan.half) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            gemm_w4a4_kernel<EPI, MODE_HALF><<<dim3((unsigned)gemm_grid(2 * (tiles - plan.full))), G_THREADS, 0, st>>>(
+                Aq, As, XO, T, d.B_q_tiles, d.B_s_rows, d.W_O, d.d_out, d.k_pad, d.k_ld, out, vec_store, q, sp);
+        }
         return hipGetLastError();
     }
     const int64_t items = plan.full + (tiles - plan.full) * plan.split;

@@ -42,10 +42,11 @@ hipError_t launch_gemm(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
 // Split-K plan of the GEMM for T tokens and N outputs (host logic): tiles [0, full)
 // run whole, each later tile as `split` K ranges whose fp32 partial sums take
 // part_bytes of workspace (`part`, 256-byte aligned; unused and may be null when
-// split == 1).
+// split == 1), or, with half set, as two 256 x 128 half tiles in a launch of their own.
 struct GemmSplit {
     int64_t full;
     int32_t split;
+    int32_t half;
     size_t part_bytes;
 };
 GemmSplit gemm_split_plan(int64_t T, int64_t N, int64_t k_pad, int64_t k_ld);

@@ -449,6 +449,25 @@ def test_split_k_is_planned_and_deterministic(T, d_in, d_out, k, layout):
     assert bool(torch.equal(Y1.view(torch.int32), Y2.view(torch.int32)))
 
 
+def test_half_tiles_match_whole_tiles():
+    """A layer with at most 128 output tiles runs as 256 x 128 half tiles; each output
+    keeps its K order and MFMA sequence, so the rows equal bit for bit those that a
+    larger call (140 whole tiles) computes for the same tokens (act-prep is per token)."""
+    _banner("half tiles against whole tiles: 256 of 17920 tokens, 1024 -> 512")
+    spec = synth.WORKLOADS[2]
+    inp = synth.layer_inputs(spec, T=17920, d_in=1024, d_out=512, k=32, T_cal=64)
+    X, Xc, W = to_dev(inp["X"]), to_dev(inp["X_cal"]), to_dev(inp["W"])
+    s, O, _, _ = B.w4a4_calibrate_scales(Xc, W, spec.alpha, 32)
+    packed = B.w4a4_pack_weights(W, s, O, 0)
+    Y = torch.empty(17920, 512, device="cuda")
+    B.w4a4_linear(X, packed, Y, B.alloc_workspace(17920, packed))
+    Xs = X[:256].contiguous()
+    Ys = torch.full((256, 512), float("nan"), device="cuda")
+    B.w4a4_linear(Xs, packed, Ys, B.alloc_workspace(256, packed))
+    torch.cuda.synchronize()
+    assert bool(torch.equal(Ys.view(torch.int32), Y[:256].view(torch.int32)))
+
+
 def test_error_paths_on_device():
     W = torch.zeros(64, 128, device="cuda")
     packed = B.w4a4_pack_weights(W, np.ones(128, np.float32), np.array([1, 2], np.int32), 0)
