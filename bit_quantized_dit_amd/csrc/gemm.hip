@@ -62,7 +62,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int G_THREADS = 512;               // 8 wavefronts: 2 per SIMD
 constexpr int BT = 256;                      // tokens per workgroup tile
 constexpr int BF = 256;                      // features per workgroup tile (the tile grid's width)
-constexpr int FT = 4;                        // 32-token MFMA tiles per wavefront (128 tokens)
 constexpr int FF = 2;                        // 32-feature MFMA tiles per wavefront (64 features)
 constexpr int ROW_BYTES = 64;                // 128 FP4 codes per row per K step
 constexpr int A_OFF = 0;                     // slot layout: A codes | B codes | A scales | B scales
@@ -71,7 +70,6 @@ constexpr int AS_OFF = (BT + BF) * ROW_BYTES;
 constexpr int BS_OFF = AS_OFF + BT * 4;
 constexpr int SLOT_BYTES = BS_OFF + BF * 4;  // 34 KiB
 constexpr int STAGES = 4;
-constexpr int DMA_PER_STAGE = 5;             // per wavefront: 2 A + 2 B 1-KiB code blocks, 1 scale block
 constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 
@@ -146,7 +144,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // 32-token MFMA tiles per wavefront, WT wavefronts along the tokens, NB B row blocks
     // of 16 rows per wavefront per step, DPS loads per wavefront per step
     constexpr int BF = MODE == MODE_HALF ? 128 : ::w4a4::BF;
-    constexpr int FT = BF == 256 ? 4 : 2;
+    constexpr int FT = BF == 256 ? 4 : 2;   // 32-token MFMA tiles per wavefront
     constexpr int WT = BT / (FT * 32);
     constexpr int NB = BF / 128;
     constexpr int DPS = 2 + NB + 1;
