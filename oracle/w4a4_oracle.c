@@ -411,15 +411,22 @@ void orc_output_full(const uint8_t* Aq, const uint8_t* As, const uint16_t* XO,
 
 /* H = bf16( gelu_tanh( bf16(Y) ) ), the activation between the FFN up
  * projection (ffn.0) and down projection (ffn.2) named in [R] sec. 3.1 and
- * sec. 3.5.  gelu_tanh(x) = 0.5 x (1 + tanh( sqrt(2/pi) (x + 0.044715 x^3) )),
- * evaluated in double and rounded once. */
+ * sec. 3.5.  gelu_tanh(x) = 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3).
+ * Since 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2z)), the same function is evaluated
+ * as x / (1 + exp(-2z)) in double and rounded once: the sum 1 + tanh(z) would
+ * cancel every digit for z below about -19 (x below about -6), where the true
+ * value is still far above the bf16 range limit.  exp(-2z) = +inf for very
+ * negative x gives a signed zero, which is the correctly rounded result there.
+ * A NaN input, and x = -inf (where the formula is -inf / inf), give the quiet
+ * NaN with the sign of x. */
 void orc_gelu_bf16(const float* Y, int64_t n, uint16_t* H)
 {
     const double c = sqrt(2.0 / 3.14159265358979323846);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         double x = orc_bf16_value(orc_bf16_round_f32(Y[i]));
-        double g = 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
-        H[i] = orc_bf16_round_double(g);
+        double z = c * (x + 0.044715 * x * x * x);
+        double g = x / (1.0 + exp(-2.0 * z));
+        H[i] = isnan(g) ? (uint16_t)(signbit(x) ? 0xFFC0u : 0x7FC0u) : orc_bf16_round_double(g);
     }
 }

@@ -101,12 +101,12 @@ def test_workload5_ffn_block(orc, mini):
     Hg = bf16_bits(H[trow])
     Ho = orc.gelu_bf16(r_up["Y"][trow].cpu().numpy()).reshape(Hg.shape)
     a, b = mini.bf16_to_f64(Hg), mini.bf16_to_f64(Ho)
-    big = np.abs(b) > 1e-6
+    big = np.abs(b) >= 2.0 ** -126     # the kernel evaluates in binary32
     assert np.all(np.abs(a[big] - b[big]) <= np.abs(b[big]) * 2.0 ** -7)
     mism = int(np.sum(Hg[big] != Ho[big]))
     _banner(f"  gelu: {mism} of {int(big.sum())} sampled elements differ by one bf16 ulp")
     assert mism <= big.sum() // 1000
-    assert np.all(np.abs(a[~big]) <= 2e-6)
+    assert np.all(np.abs(a[~big]) < 2.0 ** -126)
     # the fused up projection (GELU in the GEMM epilogue) gives the same H bit for bit
     H_fused = torch.empty_like(H)
     B.w4a4_gemm_prequantized_gelu_bf16(r_up["ws"], T, r_up["packed"], H_fused)

@@ -306,17 +306,43 @@ def test_fold_identity_exact(orc):
         assert np.array_equal(Y, ref)
 
 
-def test_fold_identity_fp64_general(orc):
-    """With general data the fold identity holds to fp32 rounding of the two steps:
-    the oracle's quantized output stays close to X W^T on the tiny workload recipe,
-    and smoothing + split beats naive W4A4 ([R] sec. 5 direction)."""
+def test_fold_identity_fp64_general(orc, mini):
+    """The fold on general data ([R] sec. 3.2 and 3.3), on the tiny workload recipe
+    with the oracle's own calibration (general s, k = 8):
+    * the premise: (X / s)(s * W) = X W in fp64 within 1e-13 relative;
+    * the oracle's act-prep codes equal mini's quantizer applied to fl32(X_J / s_J)
+      (numpy's IEEE binary32 divide, gathered by J and zero padded), and its weight
+      codes equal mini's quantizer applied to fl32(s_J * W_J);
+    * the oracle's output equals the fp64 product of mini's dequantized operands plus
+      the bf16 product of the raw outlier columns, within 1e-12 relative;
+    * smoothing + split beats naive W4A4 against X W ([R] sec. 5 direction)."""
     from bit_quantized_dit_amd import synth
     spec = synth.WORKLOADS[1]
     inp = synth.layer_inputs(spec, T=64, d_in=256, d_out=96, k=8, T_cal=64)
     X, W = inp["X"], inp["W"]
     s, O, J, *_ = orc.calibrate(inp["X_cal"], W, spec.alpha, 8)
+    assert O.size == 8 and not np.all(s == 1)
     ref = X.astype(np.float64) @ W.astype(np.float64).T
-    Y = orc.linear(X, s, O, J, orc.pack_weights(W, s, O, J, 0))
+    s64 = s.astype(np.float64)
+    folded = (X.astype(np.float64) / s64) @ (W.astype(np.float64) * s64).T
+    assert np.abs(folded - ref).max() <= 1e-13 * np.abs(ref).max()
+
+    pk = orc.pack_weights(W, s, O, J, 0)
+    Aq, As, XO = orc.act_prep(X, s, O, J)
+    K_pad = pk["K_pad"]
+    Xs = np.zeros((X.shape[0], K_pad), np.float32)
+    Xs[:, :J.size] = X[:, J] / s[J][None, :]
+    Ws = np.zeros((W.shape[0], K_pad), np.float32)
+    Ws[:, :J.size] = s[J][None, :] * W[:, J]
+    ca, sa = mini.quant_rows_1x32(Xs)
+    cb, sb = mini.quant_rows_1x32(Ws)
+    assert np.array_equal(Aq, mini.pack_nibbles(ca)) and np.array_equal(As, sa)
+    assert np.array_equal(pk["Bq"], mini.pack_nibbles(cb)) and np.array_equal(pk["Bs"], sb)
+    Y = orc.output_full(Aq, As, XO, pk)
+    want = (mini.dequant_1x32(mini.pack_nibbles(ca), sa) @ mini.dequant_1x32(mini.pack_nibbles(cb), sb).T +
+            mini.bf16_to_f64(mini.bf16_bits(X[:, O])) @ mini.bf16_to_f64(mini.bf16_bits(W[:, O])).T)
+    assert np.allclose(Y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
     one = np.ones(256, np.float32)
     Yn = orc.linear(X, one, np.zeros(0, np.int32), np.arange(256, dtype=np.int32),
                     orc.pack_weights(W, one, np.zeros(0, np.int32), np.arange(256, dtype=np.int32), 0))
@@ -541,6 +567,147 @@ def test_output_pairs_match_full(orc):
     assert np.array_equal(orc.output_pairs(Aq, As, XO, pk, ts, ns), Y[ts, ns])
 
 
+@pytest.mark.parametrize("layout", [0, 1, 2])
+@pytest.mark.parametrize("k", [0, 5])
+def test_output_any_layout_is_dequantize_then_matmul(orc, mini, layout, k):
+    """The oracle's output sum ([R] sec. 3.3 dual branch; sec. 3.4 weight scale groups)
+    in every weight layout equals numpy's fp64 matmul of independently dequantized
+    operands: mini's 1x32 dequantizer for the activations, mini's layout-aware
+    dequantizer (group scale looked up per (n, p)) for the weights, plus the bf16
+    product of the outlier columns.  d_out = 45 leaves a ragged last 32x32 tile and
+    d_in - k is not a multiple of 128, so the K padding is crossed; k = 0 with s = 1 is
+    the pure MXFP4 case."""
+    rng = np.random.default_rng(40 + 3 * layout + k)
+    T, d_in, d_out = 23, 300, 45
+    X = (rng.standard_normal((T, d_in)) * 0.5).astype(np.float32)
+    X[:, 17] *= 20.0
+    W = (rng.standard_normal((d_out, d_in)) * 0.03).astype(np.float32)
+    W[5:9, 100:140] *= 8.0        # uneven magnitudes across tiles and stripes
+    if k == 0:
+        s = np.ones(d_in, np.float32)
+        O = np.zeros(0, np.int32)
+        J = np.arange(d_in, dtype=np.int32)
+    else:
+        s, O, J, *_ = orc.calibrate(X, W, 0.6, k)
+    pk = orc.pack_weights(W, s, O, J, layout)
+    Aq, As, XO = orc.act_prep(X, s, O, J)
+    Y = orc.output_full(Aq, As, XO, pk)
+    want = mini.dequant_1x32(Aq, As) @ mini.dequant_weights(pk["Bq"], pk["Bs"], layout, d_out).T
+    if k:
+        want = want + mini.bf16_to_f64(XO) @ mini.bf16_to_f64(pk["WO"]).T
+    assert np.allclose(Y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # the scales differ across groups, so a wrong group lookup cannot pass unnoticed
+    assert len(np.unique(pk["Bs"])) >= 3
+
+
+def test_col_absmax_bf16(orc, mini):
+    """act_scale_j on bf16 activations ([R] sec. 3.2): the oracle widens each bf16 bit
+    pattern exactly, so the column maxima equal numpy's maxima of the widened values,
+    including signed zeros, subnormal bf16 values and columns whose maximum is negative
+    before |.|; a NaN or Inf anywhere is refused."""
+    rng = np.random.default_rng(41)
+    V = (rng.standard_normal((150, 67)) * rng.uniform(1e-3, 20, 67)).astype(np.float32)
+    V[:, 3] = -np.abs(V[:, 3])
+    V[:, 4] = 0.0
+    V[::2, 4] = -0.0
+    V[:, 5] = np.float32(2.0 ** -130) * rng.integers(1, 16, 150)   # bf16 subnormals
+    Xb = mini.bf16_bits(V)
+    act = orc.col_absmax(Xb)
+    want = np.abs(mini.bf16_to_f64(Xb)).max(axis=0).astype(np.float32)
+    assert np.array_equal(act.view(np.uint32), want.view(np.uint32))
+    assert act[5] > 0 and act[5] < 2.0 ** -126
+    for bad in (0x7FC0, 0xFF80):
+        Xn = Xb.copy()
+        Xn[7, 9] = bad
+        with pytest.raises(ValueError):
+            orc.col_absmax(Xn)
+
+
+def test_e8m0_every_positive_pattern(orc, mini):
+    """The E8M0 rule on every one of the 2^31 non-negative binary32 patterns (zero,
+    every subnormal, every normal, +Inf and every positive NaN): the oracle's frexp
+    formulation equals mini's bit-field formulation."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 24
+
+    def run(c):
+        a = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint32).view(np.float32)
+        x, y = orc.e8m0_codes(a), mini.e8m0(a)
+        return int(np.count_nonzero(x != y))
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        bad = sum(ex.map(run, range((1 << 31) // chunk)))
+    assert bad == 0
+
+
+def test_gelu_every_bf16_input(orc):
+    """GELU-tanh between the FFN projections ([R] sec. 3.1 and 3.5): H depends only on
+    bf16(Y), so all 65536 bf16 inputs cover it.  For every finite input the oracle's H
+    is a nearest bf16 value to 0.5 x (1 + tanh(z)), z = sqrt(2/pi)(x + 0.044715 x^3),
+    evaluated in 60-digit decimal arithmetic (tanh from its exponential definition), the
+    far negative tail included; where the exact value lies within 1e-12 (relative) of a
+    rounding boundary either neighbour is accepted.  +Inf gives +Inf, and NaN and -Inf
+    give the quiet NaN with the input's sign."""
+    from decimal import Decimal, getcontext
+    # 240 digits: for |2z| <= 400 the sum 1 + tanh(z) loses at most 174 of them
+    getcontext().prec = 240
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x32 = (pats.astype(np.uint32) << 16).view(np.float32)
+    H = orc.gelu_bf16(x32)
+    c = (Decimal(2) / Decimal("3.14159265358979323846264338327950288419716939937510")).sqrt()
+
+    def dval(p):   # exact value of a finite bf16 pattern
+        return Decimal(float((np.uint32(p) << 16).view(np.float32)))
+
+    def gelu(x):
+        z = c * (x + Decimal("0.044715") * x * x * x)
+        # beyond |2z| = 400 the factor 0.5 (1 + tanh z) is within 2 e^-400 of 0 or 1;
+        # with |x| < 2^128 the result then rounds to a signed zero or to x itself
+        if 2 * z < -400:
+            return Decimal(0) * x.copy_sign(Decimal(-1))
+        if 2 * z > 400:
+            return x
+        e = (2 * z).exp()
+        return Decimal("0.5") * x * (1 + (e - 1) / (e + 1))
+
+    bad = []
+    for p in range(1 << 16):
+        mag = p & 0x7FFF
+        if mag >= 0x7F80:
+            continue
+        g = gelu(dval(p))
+        h = int(H[p])
+        if (h & 0x7FFF) >= 0x7F80:
+            bad.append(p)
+            continue
+        hv = dval(h)
+        # neighbours of h in value order (sign-magnitude patterns)
+        neigh = []
+        for dm in (-1, 1):
+            m2 = (h & 0x7FFF) + dm
+            if m2 < 0:
+                neigh.append(dval(0x0001 | ((h & 0x8000) ^ 0x8000)))
+            elif m2 < 0x7F80:
+                neigh.append(dval((h & 0x8000) | m2))
+        dh = abs(hv - g)
+        for nv in neigh:
+            dn = abs(nv - g)
+            if dn < dh and (dh - dn) > Decimal("1e-12") * abs(g):
+                bad.append(p)
+                break
+    assert bad == [], [hex(b) for b in bad[:10]]
+    assert H[0x7F80] == 0x7F80                      # +Inf
+    assert H[0xFF80] == 0xFFC0                      # -Inf -> NaN with the sign of x
+    assert H[0x7FC0] == 0x7FC0 and H[0xFFC1] == 0xFFC0
+    # spot values: the tail reaches bf16 subnormals, and the zero signs follow x
+    assert H[0x0000] == 0x0000 and H[0x8000] == 0x8000
+    assert 0x8000 < int(H[int(mini_bits(-10.25))]) < 0x8080
+
+
+def mini_bits(v):
+    return int((np.array([v], np.float32).view(np.uint32)[0] >> 16))
+
+
 def test_gelu_against_library(orc, mini):
     """GELU-tanh between the FFN up and down projections: the oracle's double-precision
     formula rounded once to bf16 agrees with torch's float64 tanh-GELU rounded to bf16
@@ -552,8 +719,8 @@ def test_gelu_against_library(orc, mini):
     ref = torch.nn.functional.gelu(xb, approximate="tanh")
     refb = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     # Away from the far negative tail both round the same real number once to bf16.
-    # In the tail (true value below ~1e-6 in magnitude) 1 + tanh cancels and the two
-    # formulations differ in how many of its tiny digits survive; both stay tiny.
+    # In the tail (true value below ~1e-6 in magnitude) torch's 1 + tanh cancels, so
+    # only smallness is compared there (the decimal pin above covers the tail).
     r = ref.numpy()
     big = np.abs(r) > 1e-6
     assert np.mean(H[big] == refb[big]) > 0.9995
