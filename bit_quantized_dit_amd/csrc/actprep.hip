@@ -157,6 +157,9 @@ __global__ __launch_bounds__(AP_THREADS) void actprep_kernel(
     uint8_t* __restrict__ Aq, uint8_t* __restrict__ As, uint16_t* __restrict__ XO) {
     extern __shared__ float row[];
     zero_pads<AP_THREADS>(row, k_j, k_pad, k, k_ld);
+    // with k_j = 0 (per-call outliers) the zeroed range holds the J slots that other
+    // wavefronts fill for the first row: every zero lands before any phase-1 write
+    __syncthreads();
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         const XT* xr = X + t * d_in;
         for (int64_t j = threadIdx.x; j < d_in; j += AP_THREADS) {
@@ -226,6 +229,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     const int64_t row_words = lds_words(k_pad, k_ld);
     zero_pads<NT>(lds_rows, k_j, k_pad, k, k_ld);
     zero_pads<NT>(lds_rows + row_words, k_j, k_pad, k, k_ld);
+    // with k_j = 0 (per-call outliers) the zeroed range holds the J slots that other
+    // wavefronts fill for the first rows: every zero lands before any phase-1 write
+    __syncthreads();
 
     const int64_t npairs = d_in / 2;
     int32_t slot[MAXM][2];

@@ -154,6 +154,36 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+# Shape, dtype and device checks on the host side of the binding: a tensor that does
+# not match what the library will read or write would otherwise become an
+# out-of-bounds access inside a kernel.  Sizes of the workspace are checked by the
+# library itself (status W4A4_ERR_SHAPE).
+def _acts(X: torch.Tensor, d_in: int, name: str = "X") -> int:
+    _dev(X, name)
+    _x_dtype(X)
+    if X.dim() != 2 or X.shape[1] != d_in:
+        raise ValueError(f"{name} must be [T, {d_in}], got {tuple(X.shape)}")
+    return X.shape[0]
+
+
+def _out(Y: torch.Tensor, T: int, d_out: int, dtype: torch.dtype, name: str, like: torch.Tensor | None = None):
+    _dev(Y, name)
+    if Y.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {Y.dtype}")
+    if tuple(Y.shape) != (T, d_out):
+        raise ValueError(f"{name} must be [{T}, {d_out}], got {tuple(Y.shape)}")
+    if like is not None and Y.device != like.device:
+        raise ValueError(f"{name} is on {Y.device}, expected {like.device}")
+
+
+def _wsbuf(ws: torch.Tensor, like: torch.Tensor, name: str = "ws") -> None:
+    _dev(ws, name)
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 buffer, got {ws.dtype}")
+    if ws.device != like.device:
+        raise ValueError(f"{name} is on {ws.device}, expected {like.device}")
+
+
 @dataclass
 class PackedLayer:
     """A packed layer: the device blob (kept alive here) and its descriptor."""
@@ -211,9 +241,15 @@ class PackedLayer:
 
 def w4a4_column_absmax(X: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     _dev(X, "X")
+    _x_dtype(X)
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D, got {tuple(X.shape)}")
     rows, cols = X.shape
     if out is None:
         out = torch.empty(cols, dtype=torch.int32, device=X.device)
+    _dev(out, "out")
+    if out.dtype not in (torch.int32, torch.uint32) or out.numel() != cols or out.device != X.device:
+        raise ValueError(f"out must be a 32-bit integer tensor of {cols} elements on {X.device}")
     _check("w4a4_column_absmax", lib().w4a4_column_absmax(_ptr(X), _x_dtype(X), rows, cols, _ptr(out),
                                                            _stream(stream)))
     return out
@@ -305,9 +341,9 @@ def workspace_dyn_views(ws: torch.Tensor, T: int, packed: PackedLayerDyn) -> dic
 
 def w4a4_linear_dyn(X: torch.Tensor, packed: PackedLayerDyn, Y: torch.Tensor, ws: torch.Tensor,
                     stream=None) -> None:
-    _dev(X, "X")
-    _dev(Y, "Y")
-    T = X.shape[0]
+    T = _acts(X, packed.d_in)
+    _out(Y, T, packed.d_out, torch.float32, "Y", X)
+    _wsbuf(ws, X)
     st = lib().w4a4_linear_dyn(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
                                ws.numel(), _stream(stream))
     _check("w4a4_linear_dyn", st)
@@ -421,8 +457,8 @@ def workspace_views(ws: torch.Tensor, T: int, packed: PackedLayer) -> dict:
 
 
 def w4a4_quantize_activations(X: torch.Tensor, packed: PackedLayer, ws: torch.Tensor, stream=None) -> None:
-    _dev(X, "X")
-    T = X.shape[0]
+    T = _acts(X, packed.d_in)
+    _wsbuf(ws, X)
     st = lib().w4a4_quantize_activations(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(ws),
                                          ws.numel(), _stream(stream))
     _check("w4a4_quantize_activations", st)
@@ -430,7 +466,8 @@ def w4a4_quantize_activations(X: torch.Tensor, packed: PackedLayer, ws: torch.Te
 
 def w4a4_gemm_prequantized(ws: torch.Tensor, T: int, packed: PackedLayer, Y: torch.Tensor,
                            stream=None) -> None:
-    _dev(Y, "Y")
+    _out(Y, T, packed.d_out, torch.float32, "Y")
+    _wsbuf(ws, Y)
     st = lib().w4a4_gemm_prequantized(_ptr(ws), ws.numel(), T, ctypes.byref(packed.desc), _ptr(Y),
                                       _stream(stream))
     _check("w4a4_gemm_prequantized", st)
@@ -438,9 +475,9 @@ def w4a4_gemm_prequantized(ws: torch.Tensor, T: int, packed: PackedLayer, Y: tor
 
 def w4a4_linear(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, ws: torch.Tensor,
                 stream=None) -> None:
-    _dev(X, "X")
-    _dev(Y, "Y")
-    T = X.shape[0]
+    T = _acts(X, packed.d_in)
+    _out(Y, T, packed.d_out, torch.float32, "Y", X)
+    _wsbuf(ws, X)
     st = lib().w4a4_linear(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
                            ws.numel(), _stream(stream))
     _check("w4a4_linear", st)
@@ -448,9 +485,8 @@ def w4a4_linear(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, ws: torch
 
 def w4a4_gemm_prequantized_gelu_bf16(ws: torch.Tensor, T: int, packed: PackedLayer, H: torch.Tensor,
                                      stream=None) -> None:
-    _dev(H, "H")
-    if H.dtype != torch.bfloat16:
-        raise TypeError("H must be bfloat16")
+    _out(H, T, packed.d_out, torch.bfloat16, "H")
+    _wsbuf(ws, H)
     st = lib().w4a4_gemm_prequantized_gelu_bf16(_ptr(ws), ws.numel(), T, ctypes.byref(packed.desc), _ptr(H),
                                                 _stream(stream))
     _check("w4a4_gemm_prequantized_gelu_bf16", st)
@@ -458,11 +494,9 @@ def w4a4_gemm_prequantized_gelu_bf16(ws: torch.Tensor, T: int, packed: PackedLay
 
 def w4a4_linear_gelu_bf16(X: torch.Tensor, packed: PackedLayer, H: torch.Tensor, ws: torch.Tensor,
                           stream=None) -> None:
-    _dev(X, "X")
-    _dev(H, "H")
-    if H.dtype != torch.bfloat16:
-        raise TypeError("H must be bfloat16")
-    T = X.shape[0]
+    T = _acts(X, packed.d_in)
+    _out(H, T, packed.d_out, torch.bfloat16, "H", X)
+    _wsbuf(ws, X)
     st = lib().w4a4_linear_gelu_bf16(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(H), _ptr(ws),
                                       ws.numel(), _stream(stream))
     _check("w4a4_linear_gelu_bf16", st)
@@ -471,6 +505,10 @@ def w4a4_linear_gelu_bf16(X: torch.Tensor, packed: PackedLayer, H: torch.Tensor,
 def w4a4_gelu_tanh_bf16(Y: torch.Tensor, H: torch.Tensor, stream=None) -> None:
     _dev(Y, "Y")
     _dev(H, "H")
+    if Y.dtype != torch.float32 or H.dtype != torch.bfloat16:
+        raise TypeError(f"Y must be float32 and H bfloat16, got {Y.dtype} and {H.dtype}")
+    if Y.shape != H.shape or Y.device != H.device:
+        raise ValueError(f"H must match Y's shape and device: {tuple(H.shape)} vs {tuple(Y.shape)}")
     st = lib().w4a4_gelu_tanh_bf16(_ptr(Y), Y.numel(), _ptr(H), _stream(stream))
     _check("w4a4_gelu_tanh_bf16", st)
 
@@ -502,8 +540,8 @@ def ffn_workspace_views(ws: torch.Tensor, T: int, up: PackedLayer, down: PackedL
 
 
 def w4a4_ffn_up_quantize(X: torch.Tensor, up: PackedLayer, down: PackedLayer, ws: torch.Tensor, stream=None) -> None:
-    _dev(X, "X")
-    T = X.shape[0]
+    T = _acts(X, up.d_in)
+    _wsbuf(ws, X)
     st = lib().w4a4_ffn_up_quantize(_ptr(X), _x_dtype(X), T, ctypes.byref(up.desc), ctypes.byref(down.desc),
                                     _ptr(ws), ws.numel(), _stream(stream))
     _check("w4a4_ffn_up_quantize", st)
@@ -511,9 +549,9 @@ def w4a4_ffn_up_quantize(X: torch.Tensor, up: PackedLayer, down: PackedLayer, ws
 
 def w4a4_ffn_forward(X: torch.Tensor, up: PackedLayer, down: PackedLayer, Y: torch.Tensor, ws: torch.Tensor,
                      stream=None) -> None:
-    _dev(X, "X")
-    _dev(Y, "Y")
-    T = X.shape[0]
+    T = _acts(X, up.d_in)
+    _out(Y, T, down.d_out, torch.float32, "Y", X)
+    _wsbuf(ws, X)
     st = lib().w4a4_ffn_forward(_ptr(X), _x_dtype(X), T, ctypes.byref(up.desc), ctypes.byref(down.desc), _ptr(Y),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check("w4a4_ffn_forward", st)

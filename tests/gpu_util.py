@@ -123,6 +123,33 @@ def _check_act(orc, r, X, rows=None):
     return Aq_o, As_o, XO_o
 
 
+def check_act_all_rows(orc, views, X, s, O, J, chunk=8192, what="act-prep"):
+    """Every token row of the GPU's activation codes, scales and X_O equal the
+    oracle's act-prep of the same rows ([R] sec. 3.2 and 3.3), bit for bit.  X is a
+    host array (fp32, or bf16 bit patterns in uint16) or a device bf16 tensor (the
+    GPU's own H, fed to the oracle as it is).  The comparison runs in chunks of rows
+    so that the host never holds more than one chunk of codes."""
+    T = views["A_s"].shape[0]
+    k = O.size
+    aq_all, as_all, xo_all = views["A_q"], views["A_s"], views["X_O"]
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        Xc = X[t0:t1]
+        if isinstance(Xc, torch.Tensor):
+            Xc = bf16_bits(Xc)
+        Aq_o, As_o, XO_o = orc.act_prep(Xc, s, O, J)
+        assert np.array_equal(u8(as_all[t0:t1]), As_o), f"{what}: A_s differs in rows {t0}..{t1 - 1}"
+        aq = u8(aq_all[t0:t1])
+        if not np.array_equal(aq, Aq_o):
+            r, c = np.argwhere(aq != Aq_o)[0]
+            raise AssertionError(f"{what}: A_q differs first at row {t0 + r}, byte {c}: "
+                                 f"{aq[r, c]:#04x} vs {Aq_o[r, c]:#04x}")
+        if k:
+            xo = bf16_bits(xo_all[t0:t1])
+            assert np.array_equal(xo[:, :k], XO_o), f"{what}: X_O differs in rows {t0}..{t1 - 1}"
+            assert not xo[:, k:].any(), f"{what}: X_O padding columns not zero"
+
+
 def _check_y_full(orc, r, X):
     Aq_o, As_o, XO_o = _check_act(orc, r, X)
     Yref = orc.output_full(Aq_o, As_o, XO_o, r["pk_o"])

@@ -487,13 +487,32 @@ def test_error_paths_on_device():
     with pytest.raises(B.W4A4Error) as e:
         B.w4a4_linear(big[1:1281].view(10, 128), packed, Y, ws)
     assert e.value.status == 3
+    # the binding refuses tensors that do not match what the kernels read or write,
+    # before anything reaches the library
+    with pytest.raises(ValueError):
+        B.w4a4_linear(torch.zeros(10, 127, device="cuda"), packed, Y, ws)
+    with pytest.raises(ValueError):
+        B.w4a4_linear(X, packed, torch.empty(10, 63, device="cuda"), ws)
+    with pytest.raises(TypeError):
+        B.w4a4_linear(X, packed, torch.empty(10, 64, device="cuda", dtype=torch.bfloat16), ws)
+    with pytest.raises(TypeError):
+        B.w4a4_linear(X, packed, Y, ws.view(torch.int32))
+    with pytest.raises(ValueError):
+        B.w4a4_gemm_prequantized(ws, 11, packed, Y)
+    with pytest.raises(TypeError):
+        B.w4a4_linear_gelu_bf16(X, packed, Y, ws)
+    with pytest.raises(ValueError):
+        B.w4a4_gelu_tanh_bf16(Y, torch.empty(10, 32, device="cuda", dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        B.w4a4_gelu_tanh_bf16(Y.to(torch.bfloat16), torch.empty(10, 64, device="cuda", dtype=torch.bfloat16))
 
 
 def test_gelu_kernel(orc, mini):
     """GPU GELU-tanh in fp32 vs the oracle's double-precision formula: at most one bf16
-    ulp apart wherever the exact value is in the binary32 normal range (the kernel
-    evaluates in binary32, so below 2^-126 it may give a signed zero), and the mismatch
-    count is small."""
+    ulp apart wherever |GELU| >= 2^-120, and the mismatch count is small.  The kernel
+    evaluates x / (1 + exp(-2z)) in binary32, whose exp overflows once the exact result
+    is below |x| 2^-128 (< 2^-124 here): such results come out as a signed zero, so
+    below 2^-120 only smallness and the sign are checked."""
     rng = np.random.default_rng(70)
     Yh = np.concatenate([rng.standard_normal(1 << 20) * 3, np.linspace(-12, 12, 4097),
                          np.linspace(-10.5, -5, 4097)]).astype(np.float32)
@@ -504,10 +523,10 @@ def test_gelu_kernel(orc, mini):
     ref = orc.gelu_bf16(Yh)
     a = mini.bf16_to_f64(got)
     b = mini.bf16_to_f64(ref)
-    big = np.abs(b) >= 2.0 ** -126
+    big = np.abs(b) >= 2.0 ** -120
     ulp = np.abs(b[big]) * 2.0 ** -7
     assert np.all(np.abs(a[big] - b[big]) <= ulp)
-    assert np.all(np.abs(a[~big]) < 2.0 ** -126)
+    assert np.all(np.abs(a[~big]) < 2.0 ** -120)
     assert np.all(np.signbit(a) == np.signbit(b))
     mism = int(np.sum(got[big] != ref[big]))
     _banner(f"gelu mismatches: {mism} of {int(big.sum())}")

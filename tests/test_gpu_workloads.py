@@ -1,11 +1,14 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (w4a4_linear on the whole token batch).
 
-Where the oracle cannot redo a whole workload in seconds, it recomputes sampled
-token rows of the activation codes and sampled outputs one by one; codes are compared
-bit-exactly, outputs with the GEMM tolerance.  The FFN block is checked stage by stage:
-up-projection, GELU (oracle applied to the GPU's Y_up), down act-prep (oracle applied
-to the GPU's H) and down output.
+Activation codes, scales and X_O are compared bit for bit with the oracle's act-prep on
+every token row of every workload (in chunks at 57600 tokens).  Outputs are compared
+with the GEMM tolerance: all of them at the tiny workload, sampled (row, feature) pairs
+and whole rows elsewhere, where the oracle's fp64 sum of all outputs would take
+minutes.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
+to the GPU's Y_up), down act-prep (oracle applied to the GPU's H, every row) and down
+output; the fully fused block's down codes are checked against the oracle's act-prep of
+the H that the unfused chain produces through the same layer, every row.
 """
 import numpy as np
 import pytest
@@ -14,7 +17,7 @@ import torch
 from bit_quantized_dit_amd import synth
 from bit_quantized_dit_amd import w4a4 as B
 from tests.gpu_util import (_banner, _check_act, _check_packed, _check_y_full, _layer,
-                            assert_y_close, bf16_bits, to_dev, u8)
+                            assert_y_close, bf16_bits, check_act_all_rows, to_dev, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +81,8 @@ def test_workload4_57600_tokens(orc):
     assert np.all(heavy_max > 6.0)     # every heavy column reaches max |x| > 6
     r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, spec.k, spec.layout)
     _check_packed(r)
+    check_act_all_rows(orc, B.workspace_views(r["ws"], r["T"], r["packed"]), inp["X"], r["s"], r["O"], r["J"])
+    _banner(f"  act-prep: all {r['T']} rows bit-exact")
     st, _ = _check_sampled(orc, r, inp["X"], np.random.default_rng(4))
     _banner(f"  {st}")
 
@@ -88,6 +93,9 @@ def test_workload5_ffn_block(orc, mini):
     inp = synth.layer_inputs(up)
     r_up = _layer(orc, inp["X"], inp["X_cal"], inp["W"], up.alpha, up.k, up.layout)
     _check_packed(r_up)
+    check_act_all_rows(orc, B.workspace_views(r_up["ws"], r_up["T"], r_up["packed"]), inp["X"], r_up["s"],
+                       r_up["O"], r_up["J"], what="up act-prep")
+    _banner(f"  up act-prep: all {r_up['T']} rows bit-exact")
     rng = np.random.default_rng(5)
     st_up, _ = _check_sampled(orc, r_up, inp["X"], rng)
     _banner(f"  up: {st_up}")
@@ -101,12 +109,12 @@ def test_workload5_ffn_block(orc, mini):
     Hg = bf16_bits(H[trow])
     Ho = orc.gelu_bf16(r_up["Y"][trow].cpu().numpy()).reshape(Hg.shape)
     a, b = mini.bf16_to_f64(Hg), mini.bf16_to_f64(Ho)
-    big = np.abs(b) >= 2.0 ** -126     # the kernel evaluates in binary32
+    big = np.abs(b) >= 2.0 ** -120     # below, the kernel's binary32 exp overflows to a signed zero
     assert np.all(np.abs(a[big] - b[big]) <= np.abs(b[big]) * 2.0 ** -7)
     mism = int(np.sum(Hg[big] != Ho[big]))
     _banner(f"  gelu: {mism} of {int(big.sum())} sampled elements differ by one bf16 ulp")
     assert mism <= big.sum() // 1000
-    assert np.all(np.abs(a[~big]) < 2.0 ** -126)
+    assert np.all(np.abs(a[~big]) < 2.0 ** -120)
     # the fused up projection (GELU in the GEMM epilogue) gives the same H bit for bit
     H_fused = torch.empty_like(H)
     B.w4a4_gemm_prequantized_gelu_bf16(r_up["ws"], T, r_up["packed"], H_fused)
@@ -134,13 +142,11 @@ def test_workload5_ffn_block(orc, mini):
     r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y, "T": T,
          "pk_o": orc.pack_weights(Wd, s, O, J, down.layout)}
     _check_packed(r)
+    check_act_all_rows(orc, B.workspace_views(ws, T, packed), H, s, O, J, what="down act-prep")
+    _banner(f"  down act-prep of the GPU's H: all {T} rows bit-exact (codes, scales, X_O)")
     drows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 128)]))
     Hs = bf16_bits(H[torch.as_tensor(drows, device="cuda")])
     Aq_o, As_o, XO_o = orc.act_prep(Hs, s, O, J)
-    v = B.workspace_views(ws, T, packed)
-    dsel = torch.as_tensor(drows, device="cuda")
-    assert np.array_equal(v["A_s"][dsel].cpu().numpy(), As_o)
-    assert np.array_equal(v["A_q"][dsel].cpu().numpy(), Aq_o)
     ts_l, ns = _sample_pairs(rng, drows.size, down.d_out, 4096, full_rows=(0,))
     Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts_l, ns)
     Ysel = Y[torch.as_tensor(drows[ts_l], device="cuda"), torch.as_tensor(ns, device="cuda")]
@@ -166,12 +172,14 @@ def test_workload5_ffn_block(orc, mini):
     B.w4a4_quantize_activations(Hq, packed, wsd)
     Y2 = torch.empty(T, down.d_out, dtype=torch.float32, device="cuda")
     B.w4a4_gemm_prequantized(wsd, T, packed, Y2)
-    del Hq
     wsf = B.alloc_workspace_ffn(T, up_p, packed)
     Yf = torch.empty_like(Y2)
     B.w4a4_ffn_forward(Xd, up_p, packed, Yf, wsf)
     torch.cuda.synchronize()
     fz, rf = B.ffn_workspace_views(wsf, T, up_p, packed), B.workspace_views(wsd, T, packed)
+    # the fused epilogue's codes against the oracle's act-prep of the same H, every row
+    check_act_all_rows(orc, fz, Hq, s, O, J, what="fused down act-prep")
+    del Hq
     assert bool(torch.equal(fz["A_s"], rf["A_s"])), "fused A_s differs"
     assert bool(torch.equal(fz["A_q"], rf["A_q"])), "fused A_q differs"
     assert bool(torch.equal(fz["X_O"].view(torch.int16), rf["X_O"].view(torch.int16))), "fused X_O differs"
