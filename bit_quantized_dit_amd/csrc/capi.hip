@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -211,6 +212,7 @@ const char* w4a4_status_string(int status) {
         case W4A4_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case W4A4_ERR_DEVICE: return "HIP runtime error";
         case W4A4_ERR_NONFINITE: return "non-finite calibration data";
+        case W4A4_ERR_SCRATCH: return "workspace needed exceeds the fixed scratch of w4a4_linear_noalloc";
         default: return "unknown status";
     }
 }
@@ -650,3 +652,44 @@ int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream) {
 }
 
 }  // extern "C"
+
+// The fixed workspace of w4a4_linear_noalloc.  Each device holds its own copy of this
+// array; in host code its name is only a stand-in, so every host use goes through the
+// device address looked up below.
+static __device__ __align__(256) uint8_t scratch[W4A4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device with
+// that device current.
+int scratch_on_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4A4_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4A4_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" int w4a4_linear_noalloc(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
+                                   void* stream) {
+    if (T < 0) return W4A4_ERR_INVALID;
+    int st = check_desc(desc);
+    if (st) return st;
+    if (T == 0) return W4A4_OK;
+    if (ws_layout(T, desc).total > W4A4_NOALLOC_SCRATCH_BYTES) return W4A4_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st) return st;
+    return linear_into(X, x_dtype, T, desc, Y, false, ws, W4A4_NOALLOC_SCRATCH_BYTES, stream);
+}

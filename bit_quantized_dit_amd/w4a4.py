@@ -23,7 +23,8 @@ W4A4_WS_1X32 = 0
 W4A4_WS_32X32_TILE = 1
 W4A4_WS_128X1_STRIPE = 2
 STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR_ALIGN",
-          4: "W4A4_ERR_DEVICE", 5: "W4A4_ERR_NONFINITE"}
+          4: "W4A4_ERR_DEVICE", 5: "W4A4_ERR_NONFINITE", 6: "W4A4_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 128 << 20    # W4A4_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", "w4a4_packed_size",
            "w4a4_pack_weights", "w4a4_workspace_layout", "w4a4_workspace_size",
@@ -31,7 +32,8 @@ EXPORTS = ("w4a4_status_string", "w4a4_column_absmax", "w4a4_calibrate_scales", 
            "w4a4_gemm_prequantized_gelu_bf16", "w4a4_linear_gelu_bf16", "w4a4_gelu_tanh_bf16",
            "w4a4_search_scratch_size", "w4a4_search_alpha_k", "w4a4_packed_dyn_size", "w4a4_pack_weights_dyn",
            "w4a4_workspace_dyn_layout", "w4a4_workspace_dyn_size", "w4a4_linear_dyn",
-           "w4a4_ffn_workspace_layout", "w4a4_ffn_workspace_size", "w4a4_ffn_up_quantize", "w4a4_ffn_forward")
+           "w4a4_ffn_workspace_layout", "w4a4_ffn_workspace_size", "w4a4_ffn_up_quantize", "w4a4_ffn_forward",
+           "w4a4_linear_noalloc")
 
 
 class W4A4Packed(ctypes.Structure):
@@ -108,6 +110,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_ffn_workspace_size": (ci, [i64, P(W4A4Packed), P(W4A4Packed), P(sz)]),
             "w4a4_ffn_up_quantize": (ci, [vp, ci, i64, P(W4A4Packed), P(W4A4Packed), vp, sz, vp]),
             "w4a4_ffn_forward": (ci, [vp, ci, i64, P(W4A4Packed), P(W4A4Packed), vp, vp, sz, vp]),
+            "w4a4_linear_noalloc": (ci, [vp, ci, i64, P(W4A4Packed), vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -481,6 +484,16 @@ def w4a4_linear(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, ws: torch
     st = lib().w4a4_linear(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _ptr(ws),
                            ws.numel(), _stream(stream))
     _check("w4a4_linear", st)
+
+
+def w4a4_linear_noalloc(X: torch.Tensor, packed: PackedLayer, Y: torch.Tensor, stream=None) -> None:
+    """w4a4_linear with the workspace in the library's fixed device scratch (for callers
+    that cannot allocate); raises W4A4Error with W4A4_ERR_SCRATCH when T tokens need
+    more than NOALLOC_SCRATCH_BYTES."""
+    T = _acts(X, packed.d_in)
+    _out(Y, T, packed.d_out, torch.float32, "Y", X)
+    st = lib().w4a4_linear_noalloc(_ptr(X), _x_dtype(X), T, ctypes.byref(packed.desc), _ptr(Y), _stream(stream))
+    _check("w4a4_linear_noalloc", st)
 
 
 def w4a4_gemm_prequantized_gelu_bf16(ws: torch.Tensor, T: int, packed: PackedLayer, H: torch.Tensor,

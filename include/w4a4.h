@@ -35,7 +35,8 @@
  *   - Device pointers handed to the per-call entry points must be 16-byte
  *     aligned; buffers sized by the size queries are 256-byte aligned inside.
  *   - Calls on different streams that share a workspace race; the library keeps
- *     no global state and is otherwise reentrant.
+ *     no global state and is otherwise reentrant (the one exception is the fixed
+ *     device scratch array of w4a4_linear_noalloc).
  *   - The async per-call entry points enqueue kernels only: no allocation, no
  *     memset or copy, no synchronisation (memory that must start at zero is
  *     cleared by a kernel).  They may be captured into a HIP graph once the same
@@ -57,7 +58,9 @@ typedef enum w4a4_status {
     W4A4_ERR_SHAPE = 2,     /* size beyond the supported range, or a blob/workspace that is too small */
     W4A4_ERR_ALIGN = 3,     /* a device pointer that is not 16-byte aligned */
     W4A4_ERR_DEVICE = 4,    /* a HIP runtime error from a launch, copy or synchronisation */
-    W4A4_ERR_NONFINITE = 5  /* calibration data holds NaN or Inf */
+    W4A4_ERR_NONFINITE = 5, /* calibration data holds NaN or Inf */
+    W4A4_ERR_SCRATCH = 6    /* w4a4_linear_noalloc: the call needs more workspace than
+                               W4A4_NOALLOC_SCRATCH_BYTES */
 } w4a4_status;
 
 enum { W4A4_X_F32 = 0, W4A4_X_BF16 = 1 };
@@ -315,6 +318,23 @@ int w4a4_linear_gelu_bf16(const void* X, int x_dtype, int64_t T, const w4a4_pack
  * 0.5x(1+tanh(sqrt(2/pi)(x+0.044715x^3))) in fp32.  Y device fp32 [n], H device
  * bf16 [n].  Async. */
 int w4a4_gelu_tanh_bf16(const float* Y, int64_t n, uint16_t* H, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): w4a4_linear with its
+ * workspace in a fixed device array that the library holds on every GPU it runs on,
+ * W4A4_NOALLOC_SCRATCH_BYTES long, until the process ends.  The caller still passes X
+ * and Y (as for w4a4_linear).  The call makes no allocation and frees nothing; its
+ * first call on a device looks up that device's copy of the array.
+ *   - T tokens need w4a4_workspace_size(T, desc) bytes of it; a larger need returns
+ *     W4A4_ERR_SCRATCH before anything is enqueued.
+ *   - The results are those of w4a4_linear, bit for bit (same kernels, same plan).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on
+ *     one GPU (other streams, other host threads) race and give undefined results.
+ *     Nothing in the array needs to start at zero; it keeps the last call's contents.
+ * Async on `stream`. */
+#define W4A4_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int w4a4_linear_noalloc(const void* X, int x_dtype, int64_t T, const w4a4_packed* desc, float* Y,
+                        void* stream);
 
 #ifdef __cplusplus
 }
