@@ -252,20 +252,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
 
     constexpr int D = ap_depth<XT, MAXM>();
     typedef typename Pair<XT>::raw raw;
-    // Each workgroup owns a contiguous range of tokens, so the 4-byte A_s slots of
-    // neighbouring tokens (one 64-byte line per 16 tokens and step) are written from
-    // one CU and one L2 rather than as partial lines from several XCDs.
-    const int64_t per_wg = (T + gridDim.x - 1) / gridDim.x;
-    const int64_t t_begin = (int64_t)blockIdx.x * per_wg;
-    const int64_t t_end = min(T, t_begin + per_wg);
-    if (t_begin >= t_end) return;
+    // Tokens are dealt so that a line of the outputs fills within one round of rows in
+    // one L2: workgroup b runs on XCD b % 8 (workgroups are dispatched round-robin over
+    // the 8 XCDs), XCD x quantizes the 32-token groups g with g % 8 == x, and its
+    // G / 8 workgroups take consecutive tokens of those groups in each round (row r of
+    // workgroup b is position f = r G/8 + b/8 of the XCD's token sequence).  The 32
+    // tokens that share a 128-byte line of A_s (one step's 4 scale bytes per token), and
+    // the two tokens that share a line of the tiled A_q, are then written by workgroups
+    // of one XCD within the same round, and the line reaches memory whole.  With a
+    // contiguous token range per workgroup an A_s line stayed open across 32 rounds of
+    // streaming traffic and was written back in pieces.  (A grid that is not a multiple
+    // of 8 deals the tokens round-robin: row r of workgroup b is token r G + b.)
+    const bool by_xcd = gridDim.x % 8 == 0;
+    const int64_t gx = by_xcd ? gridDim.x / 8 : gridDim.x;
+    const int64_t wx = by_xcd ? blockIdx.x / 8 : blockIdx.x;
+    const int64_t xcd = by_xcd ? blockIdx.x % 8 : 0;
+    auto tok = [&](int64_t r) __attribute__((always_inline)) {
+        const int64_t f = r * gx + wx;
+        return by_xcd ? ((((f >> 5) << 3) + xcd) << 5) + (f & 31) : f;
+    };
+    if (tok(0) >= T) return;
     const int row_bytes = (int)(d_in * (int64_t)sizeof(XT));
     auto fetch = [&](raw (*xv)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t t = t_begin + r0 + d;
+            const int64_t t = tok(r0 + d);
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(X + (t < t_end ? t : t_begin) * d_in), 0, t < t_end ? row_bytes : 0, 0x00020000);
+                (void*)(X + (t < T ? t : 0) * d_in), 0, t < T ? row_bytes : 0, 0x00020000);
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
                 xv[d][m] = Pair<XT>::load(rs, (int32_t)((threadIdx.x + NT * m) * 2 * sizeof(XT)));
@@ -276,8 +289,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     auto batch = [&](raw (*xv)[MAXM], raw (*xn)[MAXM], int64_t r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t t = t_begin + r0 + d;
-            if (t >= t_end) break;
+            const int64_t t = tok(r0 + d);
+            if (t >= T) break;
             float* const row = lds_rows + ((r0 + d) & 1) * row_words;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
@@ -296,9 +309,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ac
     };
     raw xa[D][MAXM], xb[D][MAXM];
     fetch(xa, 0);
-    for (int64_t r = 0; t_begin + r < t_end; r += 2 * D) {
+    for (int64_t r = 0; tok(r) < T; r += 2 * D) {
         batch(xa, xb, r);
-        if (t_begin + r + D >= t_end) break;
+        if (tok(r + D) >= T) break;
         batch(xb, xa, r + D);
     }
 }
