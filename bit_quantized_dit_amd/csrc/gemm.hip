@@ -411,7 +411,52 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
     // bytes.
     constexpr int SROW = 64 + 4;   // staged row stride in floats (16 bytes of padding)
     static_assert((G_THREADS / 64) * 16 * SROW * 4 <= SLOT_BYTES, "staging fits one ring slot");
+    // fp32 Y: one 32 x 32 MFMA tile per wavefront at a time, all lanes writing; rows of
+    // 128 bytes with the 16-byte chunk c of row r at chunk position c ^ ((r / 2) % 8), so
+    // that the writes (a row per lane) and the reads (eight lanes per row) of any 16
+    // consecutive lanes fall in distinct banks; each store instruction then writes 8 rows
+    // x 128 contiguous bytes, i.e. whole cache lines.
+    auto epilogue_f32 = [&](const Tile& tl, int g) __attribute__((always_inline)) {
+        float* stage = reinterpret_cast<float*>(smem + (g & (STAGES - 1)) * SLOT_BYTES) + wave * (32 * 32);
+        const bool full = rows_a_of(tl) == BT && rows_b_of(tl) == BF && vec_store;
+        const int rr = lane >> 3, cc = lane & 7;   // the reading lane's row (mod 8) and chunk
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+#pragma unroll
+            for (int i = 0; i < FF; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f*>(stage + l32 * 32 + (((2 * q + lh) ^ ((l32 >> 1) & 7)) << 2)) =
+                        v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = rr + 8 * k;
+                    const v4f v = *reinterpret_cast<const v4f*>(stage + r * 32 + ((cc ^ ((r >> 1) & 7)) << 2));
+                    const int64_t t = tl.t0 + wt * (FT * 32) + j * 32 + r;
+                    const int64_t n = tl.f0 + wf * 64 + i * 32 + cc * 4;
+                    if (full) {
+                        __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(Y + t * N + n));
+                    } else if (t < T) {
+                        if (vec_store && n + 3 < N) {
+                            __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(Y + t * N + n));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N) Y[t * N + n + e] = v[e];
+                        }
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next tile overwrites it
+            }
+        }
+    };
+    static_assert((G_THREADS / 64) * 32 * 32 * 4 <= SLOT_BYTES, "fp32 staging fits one ring slot");
     auto epilogue = [&](const Tile& tl, int g) __attribute__((always_inline)) {
+        if constexpr (EPI == EPI_F32) {
+            epilogue_f32(tl, g);
+            return;
+        }
         float* stage = reinterpret_cast<float*>(smem + (g & (STAGES - 1)) * SLOT_BYTES) + wave * (16 * SROW);
         const bool full = rows_a_of(tl) == BT && rows_b_of(tl) == BF && vec_store;
 #pragma unroll
