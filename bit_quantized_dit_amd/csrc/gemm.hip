@@ -52,6 +52,8 @@
 #include "w4a4_device.h"
 #include "w4a4_internal.h"
 
+#include <type_traits>
+
 namespace w4a4 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -543,15 +545,18 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
             rs[tid] = f < kj ? qd.rinv[f] : 0.0;
         }
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < FF; ++i) {
+        // One 32-feature block (MFMA tile column i) for the wavefront's FT token tiles.
+        // ALL_J: every feature of the block is a J position (the common case): no
+        // masking, no X_O stores, and GELU without its NaN canonicalization, since a NaN
+        // of any payload encodes the same (scale 0xFF, zero nibbles).
+        auto quant_block = [&](auto all_j_c, int i) __attribute__((always_inline)) {
+            constexpr bool ALL_J = decltype(all_j_c)::value;
             const int64_t fb = tl.f0 + wf * 64 + i * 32;   // the block's first feature (wave-uniform)
-            if (fb >= N) continue;
             // the lane's features are fb + o, o = 4 lh + 8q + e in [0, 32); the J
             // positions among them are o < jl
             const int64_t jlo = kj - fb;
-            const bool has_j = jlo > 0, all_j = jlo >= 32;
-            const int jl = has_j ? (all_j ? 32 : (int)jlo) : 0;
+            const bool has_j = ALL_J || jlo > 0;
+            const int jl = ALL_J ? 32 : (jlo > 0 ? (jlo >= 32 ? 32 : (int)jlo) : 0);
             const double* const rl = rs + (wf * 64 + i * 32 + 4 * lh);   // the lane's first feature in the tile
 #pragma unroll
             for (int j = 0; j < FT; ++j) {
@@ -560,8 +565,13 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                 uint32_t hw[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    hw[2 * q] = gelu_tanh_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                    hw[2 * q + 1] = gelu_tanh_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    if constexpr (ALL_J) {
+                        hw[2 * q] = gelu_tanh_bf16x2_raw(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                        hw[2 * q + 1] = gelu_tanh_bf16x2_raw(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    } else {
+                        hw[2 * q] = gelu_tanh_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                        hw[2 * q + 1] = gelu_tanh_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    }
                 }
                 if (has_j) {
                     float qv[16];
@@ -575,7 +585,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                             const uint32_t w = hw[r / 2];
                             const float x = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
                             qv[r] = (float)((double)x * rr[e]);
-                            if (!all_j) qv[r] = 4 * lh + 8 * q + e < jl ? qv[r] : 0.0f;
+                            if constexpr (!ALL_J) qv[r] = 4 * lh + 8 * q + e < jl ? qv[r] : 0.0f;
                         }
                     }
                     float m4[4];
@@ -617,20 +627,29 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_w4a4_kernel(
                         if (lh == 0) qd.as[(((fb >> 7) * T + t) << 2) + ((fb >> 5) & 3)] = (uint8_t)code;
                     }
                 }
-                if (!all_j && tok) {
-                    // value r is feature fb + o, o = 4 lh + 8 (r / 4) + r % 4 in [0, 32); the
-                    // outlier slots are the o in [kj - fb, N - fb)
-                    const int64_t nhi = N - fb;
-                    const int o_min = jl, o_max = nhi > 32 ? 32 : (int)nhi;
-                    uint16_t* const xrow = qd.xo + t * qd.k_ld - jlo;
+                if constexpr (!ALL_J) {
+                    if (tok) {
+                        // value r is feature fb + o, o = 4 lh + 8 (r / 4) + r % 4 in [0, 32); the
+                        // outlier slots are the o in [kj - fb, N - fb)
+                        const int64_t nhi = N - fb;
+                        const int o_min = jl, o_max = nhi > 32 ? 32 : (int)nhi;
+                        uint16_t* const xrow = qd.xo + t * qd.k_ld - jlo;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int o = 4 * lh + 8 * (r / 4) + (r % 4);
-                        if (o >= o_min && o < o_max)
-                            xrow[o] = (uint16_t)((r & 1) ? (hw[r / 2] >> 16) : hw[r / 2]);
+                        for (int r = 0; r < 16; ++r) {
+                            const int o = 4 * lh + 8 * (r / 4) + (r % 4);
+                            if (o >= o_min && o < o_max)
+                                xrow[o] = (uint16_t)((r & 1) ? (hw[r / 2] >> 16) : hw[r / 2]);
+                        }
                     }
                 }
             }
+        };
+#pragma unroll
+        for (int i = 0; i < FF; ++i) {
+            const int64_t fb = tl.f0 + wf * 64 + i * 32;
+            if (fb >= N) continue;
+            if (kj - fb >= 32) quant_block(std::true_type{}, i);
+            else quant_block(std::false_type{}, i);
         }
     };
 

@@ -103,16 +103,27 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 // zero; x -> +inf gives x.  A NaN result (a NaN y, or y = -inf) is written as the quiet
 // NaN 0x7FC0 with the sign of y.  Shared by the standalone GELU kernel and the GEMM
 // epilogue that fuses it, so both give the same bits.
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
+__device__ __forceinline__ float gelu_tanh_f32_raw(float x) {
     constexpr float K0 = -2.302208198144325f, K1 = -0.1029432395800235f;
     const float e = __builtin_amdgcn_exp2f(x * __builtin_fmaf(x * x, K1, K0));
-    const float g = x * __builtin_amdgcn_rcpf(1.0f + e);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+    const float g = gelu_tanh_f32_raw(x);
     return g != g ? __uint_as_float((__float_as_uint(x) & 0x80000000u) | 0x7FC00000u) : g;
 }
 
 __device__ __forceinline__ uint32_t gelu_tanh_bf16x2(float y0, float y1) {
     const uint32_t yb = pk_bf16(y0, y1);
     return pk_bf16(gelu_tanh_f32(__uint_as_float(yb << 16)), gelu_tanh_f32(__uint_as_float(yb & 0xFFFF0000u)));
+}
+// The same pair without the NaN canonicalization (a NaN stays a NaN of some payload),
+// for values that only go on to the MXFP4 encoding: there any NaN gives its block the
+// scale code 0xFF and zero nibbles, whatever its payload, so the encoded bits are those
+// of the canonical pair.
+__device__ __forceinline__ uint32_t gelu_tanh_bf16x2_raw(float y0, float y1) {
+    const uint32_t yb = pk_bf16(y0, y1);
+    return pk_bf16(gelu_tanh_f32_raw(__uint_as_float(yb << 16)), gelu_tanh_f32_raw(__uint_as_float(yb & 0xFFFF0000u)));
 }
 
 __device__ __forceinline__ uint16_t gelu_tanh_bf16(float y) { return (uint16_t)gelu_tanh_bf16x2(y, 0.0f); }
