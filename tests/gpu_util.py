@@ -46,6 +46,23 @@ def assert_y_close(Y: np.ndarray, Yref: np.ndarray, what: str = "Y") -> dict:
     return {"max_rel": max_rel, "fro_rel": fro}
 
 
+def full_y_reference(mini, Aq, As, XO, pk, chunk: int = 1024) -> np.ndarray:
+    """The layer's whole output in fp64 from the oracle's act-prep results and packed
+    weights, as independently dequantized operands through numpy's matmul (the form
+    the CPU pins prove equal to the oracle's own output sum in every weight layout),
+    in token chunks so that a large layer stays within memory."""
+    Wd = mini.dequant_weights(pk["Bq"], pk["Bs"], pk["layout"], pk["d_out"]).T.copy()
+    WO = mini.bf16_to_f64(pk["WO"]).T.copy() if pk["k"] else None
+    T = Aq.shape[0]
+    Y = np.empty((T, pk["d_out"]), dtype=np.float64)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        Y[t0:t1] = mini.dequant_1x32(Aq[t0:t1], As[t0:t1]) @ Wd
+        if WO is not None:
+            Y[t0:t1] += mini.bf16_to_f64(XO[t0:t1]) @ WO
+    return Y
+
+
 def _banner(msg):
     print(f"[gpu-test] {msg}", flush=True)
 

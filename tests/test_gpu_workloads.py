@@ -3,9 +3,10 @@ benchmark times (w4a4_linear on the whole token batch).
 
 Activation codes, scales and X_O are compared bit for bit with the oracle's act-prep on
 every token row of every workload (in chunks at 57600 tokens).  Outputs are compared
-with the GEMM tolerance: all of them at the tiny workload, sampled (row, feature) pairs
-and whole rows elsewhere, where the oracle's fp64 sum of all outputs would take
-minutes.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
+with the GEMM tolerance: all of them at the tiny and the 4096-token workloads (the
+latter through the dequantize-then-matmul form of the output sum, which the CPU pins
+prove equal to the oracle's), sampled (row, feature) pairs and whole rows at 57600
+tokens.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
 to the GPU's Y_up), down act-prep (oracle applied to the GPU's H, every row) and down
 output; the fully fused block's down codes are checked against the oracle's act-prep of
 the H that the unfused chain produces through the same layer, every row.
@@ -17,7 +18,7 @@ import torch
 from bit_quantized_dit_amd import synth
 from bit_quantized_dit_amd import w4a4 as B
 from tests.gpu_util import (_banner, _check_act, _check_packed, _check_y_full, _layer,
-                            assert_y_close, bf16_bits, check_act_all_rows, to_dev, u8)
+                            assert_y_close, bf16_bits, check_act_all_rows, full_y_reference, to_dev, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +56,7 @@ def test_workload1_tiny_full(orc):
 
 
 @pytest.mark.parametrize("wid", [2, 3])
-def test_workload_4096_tokens(orc, wid):
+def test_workload_4096_tokens(orc, mini, wid):
     spec = synth.WORKLOADS[wid]
     _banner(f"workload {spec.name}")
     inp = synth.layer_inputs(spec)
@@ -68,6 +69,11 @@ def test_workload_4096_tokens(orc, wid):
     Yref = orc.output_pairs(Aq_o, As_o, XO_o, r["pk_o"], ts, ns)
     Ysel = r["Y"][torch.as_tensor(ts, device="cuda"), torch.as_tensor(ns, device="cuda")]
     st = assert_y_close(Ysel.cpu().numpy(), Yref)
+    # and every output: the oracle's act-prep results and packed weights through the
+    # dequantize-then-matmul form of the output sum
+    Yfull = full_y_reference(mini, Aq_o, As_o, XO_o, r["pk_o"])
+    st_full = assert_y_close(r["Y"].cpu().numpy(), Yfull, what="Y (all outputs)")
+    _banner(f"  all {Yfull.size} outputs: {st_full}")
     # the heavy columns drawn by the generator are the ones calibration selects
     overlap = np.intersect1d(r["O"], inp["heavy"]).size
     _banner(f"  {st}; heavy columns selected as O: {overlap}/{spec.k}")
