@@ -140,15 +140,25 @@ def _check_act(orc, r, X, rows=None):
     return Aq_o, As_o, XO_o
 
 
-def check_act_all_rows(orc, views, X, s, O, J, chunk=8192, what="act-prep"):
+def check_act_all_rows(orc, views, X, s, O, J, chunk=8192, what="act-prep", y_gpu=None, pk=None, mini=None):
     """Every token row of the GPU's activation codes, scales and X_O equal the
     oracle's act-prep of the same rows ([R] sec. 3.2 and 3.3), bit for bit.  X is a
     host array (fp32, or bf16 bit patterns in uint16) or a device bf16 tensor (the
     GPU's own H, fed to the oracle as it is).  The comparison runs in chunks of rows
-    so that the host never holds more than one chunk of codes."""
+    so that the host never holds more than one chunk of codes.
+
+    With y_gpu (the GPU's output, device tensor [T, d_out]), pk (the oracle's packed
+    weights) and mini, every output is also compared with the GEMM tolerance: each
+    chunk's reference is the dequantize-then-matmul form of the output sum over the
+    oracle's codes of that chunk, and the maximum and Frobenius statistics are taken
+    over all chunks.  Returns those statistics (or None)."""
     T = views["A_s"].shape[0]
     k = O.size
     aq_all, as_all, xo_all = views["A_q"], views["A_s"], views["X_O"]
+    if y_gpu is not None:
+        Wd = mini.dequant_weights(pk["Bq"], pk["Bs"], pk["layout"], pk["d_out"]).T.copy()
+        WO = mini.bf16_to_f64(pk["WO"]).T.copy() if pk["k"] else None
+        dmax = rmax = d2 = r2 = 0.0
     for t0 in range(0, T, chunk):
         t1 = min(T, t0 + chunk)
         Xc = X[t0:t1]
@@ -165,6 +175,28 @@ def check_act_all_rows(orc, views, X, s, O, J, chunk=8192, what="act-prep"):
             xo = bf16_bits(xo_all[t0:t1])
             assert np.array_equal(xo[:, :k], XO_o), f"{what}: X_O differs in rows {t0}..{t1 - 1}"
             assert not xo[:, k:].any(), f"{what}: X_O padding columns not zero"
+        if y_gpu is not None:
+            Yr = mini.dequant_1x32(Aq_o, As_o) @ Wd
+            if WO is not None:
+                Yr += mini.bf16_to_f64(XO_o) @ WO
+            Yg = y_gpu[t0:t1].cpu().numpy().astype(np.float64)
+            assert np.array_equal(np.isnan(Yg), np.isnan(Yr)), f"Y: NaN pattern differs in rows {t0}..{t1 - 1}"
+            inf = np.isinf(Yr)
+            assert np.array_equal(Yg[inf], Yr[inf]) and not np.isinf(Yg[~inf]).any(), \
+                f"Y: infinities differ in rows {t0}..{t1 - 1}"
+            fin = np.isfinite(Yr)
+            d = Yg[fin] - Yr[fin]
+            if d.size:
+                dmax = max(dmax, float(np.abs(d).max()))
+                rmax = max(rmax, float(np.abs(Yr[fin]).max()))
+                d2 += float(np.dot(d, d))
+                r2 += float(np.dot(Yr[fin], Yr[fin]))
+    if y_gpu is None:
+        return None
+    st = {"max_rel": dmax / rmax if rmax > 0 else dmax, "fro_rel": (d2 ** 0.5) / (r2 ** 0.5) if r2 > 0 else d2 ** 0.5}
+    assert st["max_rel"] <= Y_MAX_REL, f"Y (all outputs): max|dY|/max|Y| = {st['max_rel']:.3e}"
+    assert st["fro_rel"] <= Y_FRO_REL, f"Y (all outputs): relative Frobenius error {st['fro_rel']:.3e}"
+    return st
 
 
 def _check_y_full(orc, r, X):

@@ -3,10 +3,10 @@ benchmark times (w4a4_linear on the whole token batch).
 
 Activation codes, scales and X_O are compared bit for bit with the oracle's act-prep on
 every token row of every workload (in chunks at 57600 tokens).  Outputs are compared
-with the GEMM tolerance: all of them at the tiny and the 4096-token workloads (the
-latter through the dequantize-then-matmul form of the output sum, which the CPU pins
-prove equal to the oracle's), sampled (row, feature) pairs and whole rows at 57600
-tokens.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
+with the GEMM tolerance: all of them at the tiny, the 4096-token and the 57600-token
+single-layer workloads (the latter three through the dequantize-then-matmul form of the
+output sum, which the CPU pins prove equal to the oracle's, in token chunks), and
+sampled (row, feature) pairs and whole rows in the FFN block.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
 to the GPU's Y_up), down act-prep (oracle applied to the GPU's H, every row) and down
 output; the fully fused block's down codes are checked against the oracle's act-prep of
 the H that the unfused chain produces through the same layer, every row.
@@ -79,7 +79,7 @@ def test_workload_4096_tokens(orc, mini, wid):
     _banner(f"  {st}; heavy columns selected as O: {overlap}/{spec.k}")
 
 
-def test_workload4_57600_tokens(orc):
+def test_workload4_57600_tokens(orc, mini):
     spec = synth.WORKLOADS[4]
     _banner(f"workload {spec.name}")
     inp = synth.layer_inputs(spec)
@@ -87,8 +87,9 @@ def test_workload4_57600_tokens(orc):
     assert np.all(heavy_max > 6.0)     # every heavy column reaches max |x| > 6
     r = _layer(orc, inp["X"], inp["X_cal"], inp["W"], spec.alpha, spec.k, spec.layout)
     _check_packed(r)
-    check_act_all_rows(orc, B.workspace_views(r["ws"], r["T"], r["packed"]), inp["X"], r["s"], r["O"], r["J"])
-    _banner(f"  act-prep: all {r['T']} rows bit-exact")
+    st_all = check_act_all_rows(orc, B.workspace_views(r["ws"], r["T"], r["packed"]), inp["X"], r["s"], r["O"],
+                                r["J"], y_gpu=r["Y"], pk=r["pk_o"], mini=mini)
+    _banner(f"  act-prep: all {r['T']} rows bit-exact; all {r['T'] * spec.d_out} outputs: {st_all}")
     st, _ = _check_sampled(orc, r, inp["X"], np.random.default_rng(4))
     _banner(f"  {st}")
 
