@@ -3,13 +3,14 @@ benchmark times (w4a4_linear on the whole token batch).
 
 Activation codes, scales and X_O are compared bit for bit with the oracle's act-prep on
 every token row of every workload (in chunks at 57600 tokens).  Outputs are compared
-with the GEMM tolerance: all of them at the tiny, the 4096-token and the 57600-token
-single-layer workloads (the latter three through the dequantize-then-matmul form of the
-output sum, which the CPU pins prove equal to the oracle's, in token chunks), and
-sampled (row, feature) pairs and whole rows in the FFN block.  The FFN block is checked stage by stage: up-projection, GELU (oracle applied
-to the GPU's Y_up), down act-prep (oracle applied to the GPU's H, every row) and down
-output; the fully fused block's down codes are checked against the oracle's act-prep of
-the H that the unfused chain produces through the same layer, every row.
+with the GEMM tolerance on every output: at the tiny workload against the oracle's
+output sum, elsewhere (4096 and 57600 tokens, both FFN-block layers) against the
+dequantize-then-matmul form of that sum, which the CPU pins prove equal to the oracle's,
+computed in token chunks from the oracle's own codes.  The FFN block is checked stage
+by stage: up-projection, GELU (oracle applied to the GPU's Y_up), down act-prep (oracle
+applied to the GPU's H, every row) and down output; the fully fused block's down codes
+are checked against the oracle's act-prep of the H that the unfused chain produces
+through the same layer, every row.
 """
 import numpy as np
 import pytest
@@ -100,9 +101,11 @@ def test_workload5_ffn_block(orc, mini):
     inp = synth.layer_inputs(up)
     r_up = _layer(orc, inp["X"], inp["X_cal"], inp["W"], up.alpha, up.k, up.layout)
     _check_packed(r_up)
-    check_act_all_rows(orc, B.workspace_views(r_up["ws"], r_up["T"], r_up["packed"]), inp["X"], r_up["s"],
-                       r_up["O"], r_up["J"], what="up act-prep")
-    _banner(f"  up act-prep: all {r_up['T']} rows bit-exact")
+    st_all = check_act_all_rows(orc, B.workspace_views(r_up["ws"], r_up["T"], r_up["packed"]), inp["X"],
+                                r_up["s"], r_up["O"], r_up["J"], what="up act-prep", y_gpu=r_up["Y"],
+                                pk=r_up["pk_o"], mini=mini)
+    _banner(f"  up act-prep: all {r_up['T']} rows bit-exact; all {r_up['T'] * up.d_out} outputs "
+            f"(32x32-tile weight scales): {st_all}")
     rng = np.random.default_rng(5)
     st_up, _ = _check_sampled(orc, r_up, inp["X"], rng)
     _banner(f"  up: {st_up}")
@@ -149,8 +152,10 @@ def test_workload5_ffn_block(orc, mini):
     r = {"s": s, "O": O, "J": J, "packed": packed, "ws": ws, "Y": Y, "T": T,
          "pk_o": orc.pack_weights(Wd, s, O, J, down.layout)}
     _check_packed(r)
-    check_act_all_rows(orc, B.workspace_views(ws, T, packed), H, s, O, J, what="down act-prep")
-    _banner(f"  down act-prep of the GPU's H: all {T} rows bit-exact (codes, scales, X_O)")
+    st_all = check_act_all_rows(orc, B.workspace_views(ws, T, packed), H, s, O, J, what="down act-prep",
+                                y_gpu=Y, pk=r["pk_o"], mini=mini)
+    _banner(f"  down act-prep of the GPU's H: all {T} rows bit-exact (codes, scales, X_O); "
+            f"all {T * down.d_out} outputs (128x1 stripes): {st_all}")
     drows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 128)]))
     Hs = bf16_bits(H[torch.as_tensor(drows, device="cuda")])
     Aq_o, As_o, XO_o = orc.act_prep(Hs, s, O, J)
